@@ -1,0 +1,227 @@
+"""Benchmark of the hyper-connection read on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (the configuration the headline metric is quoted on): verify windows
+of T = 1..8 tokens with a pending write, 48 independent weight sets (631 MB,
+more than the 256 MB Infinity Cache) rotated per read so every read streams its
+13,148,160 weight bytes from HBM.  One step = one sweep T = 1..8 (8 reads, each
+on the next weight set).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` = weight bytes streamed per second over the
+timed sweeps (GB/s); per-T microseconds per read and the T = 8192 prefill read
+time are reported beside it.  The roofline object describes the short-window
+kernel; the CPU baseline is the plain oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WEIGHT_BYTES = 2 * 320 * 10240 * 2 + 4 * 2560 * 4   # W_down + W_up (bf16) + w_norm (fp32)
+TOKEN_BYTES_P = 4 * 2560 * 4 * 2 + 2560 * (4 + 2 + 2)  # R and pending read, mixed + images written
+HBM_PEAK_GBPS = 8000.0
+N_SETS = 48
+TS = list(range(1, 9))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's CPU time for the baseline")
+    return ap.parse_args()
+
+
+def make_sets(torch):
+    """48 weight sets and, per (T, set), the activations of the sweep (config 2)."""
+    from hyper_connection_residual_amd import workloads as wl
+    sets = []
+    for m in range(N_SETS):
+        rng = np.random.default_rng((1, m))
+        w_norm, W_down, W_up = wl.draw_weights(rng)
+        sets.append(dict(w_norm=torch.from_numpy(w_norm).cuda(),
+                         W_down=torch.from_numpy(W_down.view(np.int16)).cuda(),
+                         W_up=torch.from_numpy(W_up.view(np.int16)).cuda()))
+    acts = {}
+    for T in TS:
+        for m in range(N_SETS):
+            rng = np.random.default_rng((1, 1000 + T, m))
+            R = wl._normal_residual(rng, T, wl.N_STREAMS, wl.WIDTH)
+            P = wl._normal_residual(rng, T, wl.N_STREAMS, wl.WIDTH, 0.1)
+            acts[(T, m)] = (torch.from_numpy(R).cuda(), torch.from_numpy(P).cuda())
+    return sets, acts
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the read has no cross-GPU "
+              "exchange; see the sharding paragraph of the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hyper_connection_residual_amd import binding
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    binding.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t_gen = time.time()
+    sets, acts = make_sets(torch)
+    outs = {T: (torch.empty((T, 2560), dtype=torch.float32, device=dev),
+                torch.empty((T, 2560), dtype=torch.int16, device=dev),
+                torch.empty((T, 2560), dtype=torch.int16, device=dev)) for T in TS}
+    print("# inputs ready in %.1f s" % (time.time() - t_gen), file=sys.stderr, flush=True)
+
+    counter = [0]
+
+    def one_read(T):
+        m = counter[0] % N_SETS
+        counter[0] += 1
+        ws = sets[m]
+        R, P = acts[(T, m)]
+        o = outs[T]
+        st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2],
+                             stream.cuda_stream)
+        if st != 0:
+            raise binding.HCError(st, "hc_read")
+
+    def step():
+        for T in TS:
+            one_read(T)
+
+    # warmup, then exactly K timed steps bracketed by synchronisation
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    n_reads = args.steps * len(TS)
+    weight_gbps = n_reads * WEIGHT_BYTES / (ms_total * 1e-3) / 1e9
+    print("# timed %d steps: %.3f ms/step (event), wall %.3f s" % (args.steps, ms_per_step, wall),
+          file=sys.stderr, flush=True)
+
+    # per-T microseconds per read (300 reads each, rotating the weight sets)
+    us_per_read = {}
+    for T in TS:
+        for _ in range(10):
+            one_read(T)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(300):
+            one_read(T)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us_per_read[str(T)] = round(a.elapsed_time(b) * 1e3 / 300, 3)
+    print("# us per read by T: %s" % us_per_read, file=sys.stderr, flush=True)
+
+    # the short-window kernel's roofline over the sweep: algorithmic bytes per
+    # launch (weights + each token's R, pending and outputs) / event-timed
+    # average launch duration (back-to-back launches on this stream)
+    alg_bytes_per_step = sum(WEIGHT_BYTES + T * TOKEN_BYTES_P for T in TS)
+    achieved = alg_bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    timeouts = binding.hc_timeouts(stream)
+    if timeouts:
+        print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
+
+    prefill = None
+    if not args.no_prefill:
+        from hyper_connection_residual_amd import workloads as wl
+        inp = wl.config_inputs(4)
+        R = torch.from_numpy(inp.R).cuda()
+        w_norm = torch.from_numpy(inp.w_norm).cuda()
+        Wd = torch.from_numpy(inp.W_down.view(np.int16)).cuda()
+        Wu = torch.from_numpy(inp.W_up.view(np.int16)).cuda()
+        T = inp.T
+        o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev))
+        for _ in range(3):
+            binding.hc_read(T, R, None, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        a.record(stream)
+        for _ in range(reps):
+            binding.hc_read(T, R, None, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        prefill = {"T": T, "ms_per_read": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        print("# prefill T=8192: %.4f ms per read" % ms, file=sys.stderr, flush=True)
+        del R, Wd, Wu, o
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        from hyper_connection_residual_amd import workloads as wl
+        reads, weight_bytes, spent = 0, 0, 0.0
+        T_cycle = TS
+        i = 0
+        while spent < args.cpu_seconds:
+            T = T_cycle[i % len(T_cycle)]
+            inp = wl.config_inputs(2, T=T, weight_set=i % N_SETS)
+            t = time.perf_counter()
+            orc.oracle_read(inp.R, inp.w_norm, inp.W_down, inp.W_up, inp.pending, threads=1)
+            spent += time.perf_counter() - t
+            reads += 1
+            weight_bytes += WEIGHT_BYTES
+            i += 1
+        cpu = {"value": round(weight_bytes / spent / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": "%d oracle reads (fp64, one thread) of the T=1..8 verify-window sweep "
+                         "with pending, cycling T and weight sets, %.1f s of CPU time" % (reads, spent)}
+        print("# cpu baseline: %s" % cpu, file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "hc read µs at T=1..8 (weight GB/s vs HBM peak); fused read ms at T=8192",
+        "value": round(weight_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "verify-window sweep T=1..8 with pending write, 48 rotated weight "
+                               "sets (631 MB), one step = 8 reads",
+                   "T": TS, "weight_sets": N_SETS, "reads_per_step": len(TS),
+                   "streams": 4, "width": 2560, "rank": 320},
+        "us_per_read": us_per_read,
+        "prefill_T8192": prefill,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "timeouts": timeouts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

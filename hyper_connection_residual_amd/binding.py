@@ -1,0 +1,161 @@
+"""Thin Python binding of the C ABI in include/hc.h (libhc.so).
+
+Argument marshalling only: every step of the read runs in the HIP kernels of
+libhc.so.  PyTorch provides device memory and the current stream.  There is no
+CPU fallback: if the library is missing or the device is not a gfx950 GPU the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first: libhc.so then binds to the HIP runtime torch uses
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhc.so")
+
+HC_OK = 0
+HC_ERR_ARG = 1
+HC_ERR_ALIGN = 2
+HC_ERR_DEVICE = 3
+HC_ERR_NOMEM = 4
+HC_ERR_LAUNCH = 5
+
+# Every function the header exports, with its ctypes signature.
+_P = ctypes.c_void_p
+SIGNATURES = {
+    "hc_read": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "hc_last_hip_error": (ctypes.c_int, []),
+    "hc_dims": (None, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)]),
+    "hc_timeouts": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
+    "hc_release": (None, []),
+}
+
+_lib = None
+
+
+class HCError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d, hip error %d)" % (
+            what, hc_status_string(status), status, hc_last_hip_error()))
+        self.status = status
+
+
+def library():
+    """Load libhc.so (it must have been built: python -m hyper_connection_residual_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libhc.so is not built; run `python -m hyper_connection_residual_amd.build` "
+                "(the read has no CPU implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def hc_read(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, stream=None):
+    """hc_read of the C ABI: device tensors (or raw device pointers as ints).
+
+    Returns the status code (0 = HC_OK)."""
+    return library().hc_read(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
+                             _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
+                             _stream(stream))
+
+
+def hc_status_string(status: int) -> str:
+    return library().hc_status_string(int(status)).decode()
+
+
+def hc_last_hip_error() -> int:
+    return library().hc_last_hip_error()
+
+
+def hc_dims():
+    n, C, r, eps = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_float()
+    library().hc_dims(ctypes.byref(n), ctypes.byref(C), ctypes.byref(r), ctypes.byref(eps))
+    return n.value, C.value, r.value, eps.value
+
+
+def hc_timeouts(stream=None) -> int:
+    cnt = ctypes.c_uint32()
+    st = library().hc_timeouts(_stream(stream), ctypes.byref(cnt))
+    if st != HC_OK:
+        raise HCError(st, "hc_timeouts")
+    return cnt.value
+
+
+def hc_release() -> None:
+    library().hc_release()
+
+
+def _check(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None):
+    """The hyper-connection read on the current stream.
+
+    R, pending: float32 [T, 4, 2560]; w_norm: float32 [4, 2560];
+    W_down: bf16 bits as int16/uint16 [320, 10240] (or a torch.bfloat16 tensor);
+    W_up: [10240, 320] likewise.  Returns (mixed float32 [T, 2560],
+    bf16 image as torch.bfloat16 [T, 2560], fp16 image as torch.float16 [T, 2560]).
+    """
+    n, C, r, _ = hc_dims()
+    T = int(R.shape[0]) if R.dim() == 3 else -1
+    _check(R, "R", torch.float32, (T, n, C))
+    if T == 0:  # nothing to read: empty outputs, no launch
+        return (torch.empty((0, C), dtype=torch.float32, device=R.device),
+                torch.empty((0, C), dtype=torch.bfloat16, device=R.device),
+                torch.empty((0, C), dtype=torch.float16, device=R.device))
+    if pending is not None:
+        _check(pending, "pending", torch.float32, (T, n, C))
+    _check(w_norm, "w_norm", torch.float32, (n, C))
+    for name, W, shape in (("W_down", W_down, (r, n * C)), ("W_up", W_up, (n * C, r))):
+        if W.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("%s must hold bf16 bits (bfloat16, int16 or uint16)" % name)
+        _check(W, name, W.dtype, shape)
+    if out is None:
+        out = (torch.empty((T, C), dtype=torch.float32, device=R.device),
+               torch.empty((T, C), dtype=torch.bfloat16, device=R.device),
+               torch.empty((T, C), dtype=torch.float16, device=R.device))
+    mixed, img_bf16, img_fp16 = out
+    _check(mixed, "out_mixed", torch.float32, (T, C))
+    _check(img_bf16, "out_bf16", img_bf16.dtype, (T, C))
+    _check(img_fp16, "out_fp16", img_fp16.dtype, (T, C))
+    st = hc_read(T, R, pending, w_norm, W_down, W_up, mixed, img_bf16, img_fp16, stream)
+    if st != HC_OK:
+        raise HCError(st, "hc_read")
+    return mixed, img_bf16, img_fp16

@@ -1,0 +1,125 @@
+/*
+ * hc.h -- C ABI of the hyper-connection read on AMD Instinct MI355X (gfx950).
+ *
+ * The read, per token t (the pages: "#315 hc: the multi-token hyper-connection
+ * read split finer", "What changes" and "Exactness"; "#1370 prefill: opt-in
+ * STRATA_HC_UPMIX=1 on CUDA", "Why" and "What it does"; "#2226
+ * STRATA_HC_PERSIST=1", Summary; "#2488 sycl/A770", Summary items 1-5):
+ *
+ *   R'[t,s,c]  = fl32(R[t,s,c] + pending[t,s,c])      (pending may be absent)
+ *   rs[t,s]    = 1 / sqrt(mean_c R'[t,s,c]^2 + eps)    per token and stream
+ *   xn[t,k]    = R'[t,s,c] * w_norm[s,c] * rs[t,s]     k = s*2560 + c
+ *   lo[t,j]    = sum_k W_down[j,k] * xn[t,k]           down 10240 -> 320
+ *   up[t,k]    = sum_j W_up[k,j] * lo[t,j]             up 320 -> 10240
+ *   gated      = up                                    (identity epilogue)
+ *   mixed[t,c] = sum_{s<4} gated[t, s*2560+c] * R'[t,s,c]
+ *   out_bf16, out_fp16 = round-to-nearest-even images of the fp32 mixed
+ *
+ * with 4 streams, width 2560, rank 320 and eps = 1e-6.  Accumulation is fp32
+ * (the GPU keeps every activation fp32-exact: bf16 matrix-core products use an
+ * exact three-way bf16 split of each fp32 activation); results agree with the
+ * exact value to about 1e-7 of max|mixed| and are bitwise reproducible run to
+ * run on the same device.
+ *
+ * Memory: every pointer argument is a DEVICE pointer (hipMalloc memory or any
+ * device-accessible allocation), row-major, contiguous, 16-byte aligned.  The
+ * caller owns all of them; the library only reads R, pending, w_norm, W_down
+ * and W_up, and only writes the three outputs.  Outputs must not overlap any
+ * input or each other.  R is not updated with R'.
+ *
+ * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream).  No host synchronization; results are visible to later work on the
+ * same stream.  The library keeps a small scratch workspace per (device,
+ * stream), allocated on the first call on that stream (and grown once for a
+ * larger T on the wide path); later calls allocate nothing.  Calls on
+ * different streams never share scratch.  Calls on ONE stream are ordered by
+ * the stream and are safe.
+ *
+ * Errors: argument checks (T < 1, a null required pointer, misalignment, a
+ * device that is not gfx950) happen before anything is enqueued and leave the
+ * outputs untouched.  A failed kernel launch returns HC_ERR_LAUNCH
+ * (hc_last_hip_error() gives the hipError_t).  Device faults surface at the
+ * caller's next synchronization, as in HIP.  The single-launch short-window
+ * kernel waits on data from other workgroups with a bounded wait; if that wait
+ * ever expires (its workgroups could not all be resident at once), the call
+ * still completes, its outputs are invalid, and hc_timeouts() reports it.
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define HC_API __attribute__((visibility("default")))
+#else
+#define HC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by hc_read and the other calls. */
+#define HC_OK 0
+#define HC_ERR_ARG 1     /* T < 1, or a required pointer is NULL */
+#define HC_ERR_ALIGN 2   /* a pointer is not 16-byte aligned */
+#define HC_ERR_DEVICE 3  /* the current device is not gfx950, or a HIP query failed */
+#define HC_ERR_NOMEM 4   /* the scratch workspace could not be allocated */
+#define HC_ERR_LAUNCH 5  /* a kernel launch failed (see hc_last_hip_error) */
+
+/* Dimensions of the read. */
+#define HC_STREAMS 4
+#define HC_WIDTH 2560
+#define HC_RANK 320
+
+/*
+ * hc_read -- one hyper-connection read of T tokens.
+ *
+ *   T          number of tokens, >= 1
+ *   R          const float  [T][4][2560]   residual streams
+ *   pending    const float  [T][4][2560]   pending write added to R first, or
+ *              NULL for none (the norm and the mix both see R' = R + pending)
+ *   w_norm     const float  [4][2560]      RMS-norm weights
+ *   W_down     const uint16_t [320][10240] bf16 bit patterns
+ *   W_up       const uint16_t [10240][320] bf16 bit patterns
+ *   out_mixed  float    [T][2560]          mixed output (fp32)
+ *   out_bf16   uint16_t [T][2560]          bf16 bits, RNE of out_mixed
+ *   out_fp16   uint16_t [T][2560]          IEEE binary16 bits, RNE of out_mixed
+ *              (subnormals kept, overflow to +-inf)
+ *   stream     hipStream_t to run on (NULL = default stream)
+ *
+ * T <= 8 runs one launch (the verify-window path); larger T runs the wide
+ * (prefill) path.  Every valid T is handled; there is no fallback to return.
+ * Returns HC_OK or an HC_ERR_* code.
+ */
+HC_API int hc_read(int64_t T, const float* R, const float* pending, const float* w_norm,
+            const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+            uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
+
+/* Text for a status code (static storage; never NULL). */
+HC_API const char* hc_status_string(int status);
+
+/* The hipError_t behind the last HC_ERR_LAUNCH / HC_ERR_DEVICE / HC_ERR_NOMEM
+ * on this host thread (0 if none). */
+HC_API int hc_last_hip_error(void);
+
+/* The read's dimensions: streams, width, rank and eps (any pointer may be NULL). */
+HC_API void hc_dims(int* n, int* C, int* r, float* eps);
+
+/*
+ * hc_timeouts -- number of expired bounded waits recorded in the workspace of
+ * (current device, stream) since the last call, then resets it to zero.
+ * Synchronizes `stream`.  *count receives 0 when the stream has no workspace.
+ * Returns HC_OK or an HC_ERR_* code.
+ */
+HC_API int hc_timeouts(void* stream, uint32_t* count);
+
+/* Free every workspace the library holds on every device (synchronizes each
+ * stream that has one).  Later calls allocate again. */
+HC_API void hc_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H */
