@@ -105,6 +105,28 @@ int workspace(int dev, hipStream_t stream, Workspace** out)
     return HC_OK;
 }
 
+// The wide path's scratch, allocated on its first use on this stream.
+int wide_workspace(Workspace* ws)
+{
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (ws->wide_base)
+        return HC_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(ws->stream, &cap);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_DEVICE);
+    if (cap != hipStreamCaptureStatusNone)
+        return record(hipErrorStreamCaptureUnsupported, HC_ERR_NOMEM);
+    const size_t bytes = hc::prefill_scratch_bytes(hc::kPrefillChunk);
+    e = hipMalloc(&ws->wide_base, bytes);
+    if (e != hipSuccess) {
+        ws->wide_base = nullptr;
+        return record(e, HC_ERR_NOMEM);
+    }
+    ws->wide_bytes = bytes;
+    return HC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,18 +151,17 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
     if (st != HC_OK)
         return st;
 
-    // Short windows: one launch per 8 tokens.
-    for (int64_t t0 = 0; t0 < T; t0 += hc::kDecMaxT) {
-        const int tn = static_cast<int>(T - t0 < hc::kDecMaxT ? T - t0 : hc::kDecMaxT);
-        const size_t o_in = static_cast<size_t>(t0) * hc::kD;
-        const size_t o_out = static_cast<size_t>(t0) * hc::kWidth;
-        hipError_t e = hc::launch_decode(tn, R + o_in, pending ? pending + o_in : nullptr, w_norm,
-                                         W_down, W_up, out_mixed + o_out, out_bf16 + o_out,
-                                         out_fp16 + o_out, ws->dec, hs);
-        if (e != hipSuccess)
-            return record(e, HC_ERR_LAUNCH);
+    if (T <= hc::kDecMaxT) {  // a short window: one launch
+        hipError_t e = hc::launch_decode(static_cast<int>(T), R, pending, w_norm, W_down, W_up,
+                                         out_mixed, out_bf16, out_fp16, ws->dec, hs);
+        return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
     }
-    return HC_OK;
+    st = wide_workspace(ws);
+    if (st != HC_OK)
+        return st;
+    hipError_t e = hc::launch_prefill(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16,
+                                      out_fp16, ws->wide_base, hc::kPrefillChunk, hs);
+    return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
 }
 
 HC_API const char* hc_status_string(int status)

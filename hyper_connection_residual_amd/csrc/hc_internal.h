@@ -62,4 +62,17 @@ hipError_t launch_decode(int T, const float* R, const float* P, const float* w_n
                          uint16_t* out_bf16, uint16_t* out_fp16, const DecodeScratch& s,
                          hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Wide path (T > kDecMaxT): three launches per chunk of up to kPrefillChunk
+// tokens (down partials, lo planes, up projection with the mix epilogue).
+// ---------------------------------------------------------------------------
+constexpr int kPrefillChunk = 4096;
+
+size_t prefill_scratch_bytes(int chunk);
+
+hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
+                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                          uint16_t* out_bf16, uint16_t* out_fp16, void* scratch, int chunk,
+                          hipStream_t stream);
+
 }  // namespace hc
