@@ -42,6 +42,12 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for the baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run 5 plain device copies of 256 MiB (the reference for "
+                         "scaling the HBM byte counters of a profiler run)")
+    ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_prefill8192_hbm_bytes.md"),
+                    help="summary of the profiler's FETCH_SIZE / WRITE_SIZE runs; its figure is "
+                         "reported only if it was measured on the current kernel source")
     return ap.parse_args()
 
 
@@ -147,6 +153,20 @@ def main():
     if timeouts:
         print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
 
+    if args.calib_copy:
+        src = torch.empty(256 << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = None
+    from hyper_connection_residual_amd import rocprof_summary
+    measured = rocprof_summary.read_traffic(args.traffic_md)
+    if measured and measured[1] == rocprof_summary.source_hash():
+        traffic = measured[0]  # HBM bytes per launch, sweep average
+
     prefill = None
     if not args.no_prefill:
         from hyper_connection_residual_amd import workloads as wl
@@ -216,7 +236,8 @@ def main():
         "us_per_read": us_per_read,
         "prefill_T8192": prefill,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "timeouts": timeouts,
     }
