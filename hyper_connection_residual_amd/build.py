@@ -30,6 +30,9 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments arrive preloaded in SGPRs (the code keeps a prologue
+    # that loads them for firmware without the feature)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

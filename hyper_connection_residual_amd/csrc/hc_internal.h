@@ -16,37 +16,33 @@ constexpr float kEps = 1e-6f;
 // ---------------------------------------------------------------------------
 // Short-window path (T <= kDecMaxT): one launch of kDecWGs workgroups, one
 // per CU, each of 8 waves.  Workgroup b runs on XCD x = b % 8 (the dispatcher
-// deals workgroups to the 8 XCDs round robin; the kernel checks it).  XCD x
-// owns columns [1280 x, 1280 x + 1280) of W_down (half of stream x / 2) and
-// output columns chosen per workgroup.
-//   down waves 0-4:  workgroup (x, i = b / 8) computes slice hl = i / 4
-//     (160 columns) for rows 80 (i % 4) .. +79, 16 rows per wave;
-//   hop B (inside the XCD, through its L2): wave 0 of workgroup (x, i) sums
-//     the XCD's 8 slices for rows 10 i .. 10 i + 9 and publishes that XCD
-//     partial to device memory;
-//   hop C (across XCDs): wave 1 of workgroup (x, i) gathers the 8 XCD
-//     partials of rows 10 i .. 10 i + 9, applies each stream's rs and forms
-//     lo for those rows -- every XCD computes all of lo itself;
-//   hop D (inside the XCD): waves 0, 2, 3, 4 stage all of lo into LDS;
-//   up waves 5-7: W_up rows of 12 (workgroups 0..127) or 8 output columns,
-//     all 4 streams, then the stream mix.
-// Hand-off words are 64 bits: payload plus the launch's generation number,
-// written once with one store and polled by the consumer.
+// deals workgroups to the 8 XCDs round robin; the kernel checks it); i = b / 8.
+//   down: XCD x owns lo rows [40 x, 40 x + 40); workgroup (x, i) computes
+//     their partial dots over columns [320 i, 320 i + 320) (inside stream
+//     i / 8) with that slice's sum of squares;
+//   hop 1 (inside the XCD, through its L2): workgroups i < 20 each reduce two
+//     rows over the XCD's 32 partials, applying each stream's rs, and publish
+//     lo device-wide;
+//   hop 2 (across XCDs): every workgroup gathers all 320 values of lo;
+//   up: workgroup b owns output columns [10 b, 10 b + 10) (all 4 streams of
+//     each), then the stream mix.
+// Weight tiles (40 rows x 320 bf16 each) are loaded straight into LDS as whole
+// cache lines.  Hand-off words are 64 bits: payload plus the launch's
+// generation number, written once with one store and polled by the consumer.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 8;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
-constexpr int kDecDownWaves = 5;
 constexpr int kDecXcds = 8;
-constexpr int kDecSliceCols = 160;  // 8 slices per XCD, 64 in all
-constexpr int kDecRowsPerWG = 10;   // rows of lo each workgroup reduces (32 x 10 = 320)
+constexpr int kDecPerXcd = kDecWGs / kDecXcds;     // 32 workgroups per XCD
+constexpr int kDecRowsPerXcd = kRank / kDecXcds;   // 40 lo rows per XCD
+constexpr int kDecCols = kD / kDecPerXcd;          // 320 W_down columns per workgroup
+constexpr int kDecReducers = kDecRowsPerXcd / 2;   // 20 workgroups per XCD reduce 2 rows each
 
 struct DecodeScratch {
-    uint64_t* xs_part;   // [8 xcd][8 slice][kRank][kDecMaxT]: slice partials (XCD-local)
-    uint64_t* xs_ssq;    // [8 xcd][8 slice][kDecMaxT]: slice sums of squares (XCD-local)
-    uint64_t* g_part;    // [8 xcd][kRank][kDecMaxT]: XCD partials (device-wide)
-    uint64_t* g_ssq;     // [8 xcd][kDecMaxT]: XCD sums of squares (device-wide)
-    uint64_t* x_lo;      // [8 xcd][kDecMaxT][kRank]: lo, bf16 hi | mid << 16 | lo3 << 32 | (gen & 0xffff) << 48 (XCD-local)
+    uint64_t* part;      // [8 xcd][32 wg][40 rows][kDecMaxT]: partial dots (XCD-local)
+    uint64_t* ssq;       // [8 xcd][32 wg][kDecMaxT]: column-slice sums of squares (XCD-local)
+    uint64_t* lo;        // [kDecMaxT][kRank]: lo (device-wide)
     uint32_t* gen;       // [kDecWGs]: launches completed by each workgroup
     uint32_t* timeouts;  // [1]: expired bounded waits and misplaced workgroups
 };
