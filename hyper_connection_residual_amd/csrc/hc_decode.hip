@@ -14,37 +14,38 @@
 // gfx950 design (the pages' kernels were written for RDNA2, Turing, Ada and
 // Arc; none of their mechanics is reused):
 //
-// * 256 workgroups x 8 waves: exactly one workgroup per CU, each streaming the
-//   same 51 KB of weights: a 40-row x 320-column tile of W_down and the 40 W_up
-//   rows of its 10 output columns (4 runs of 10 consecutive rows).
+// * 256 workgroups x 8 waves, one per CU, each streaming 51 KB of weights.  A
+//   CU serves its vector memory requests in order across its waves (measured:
+//   a load that hits L2 in 0.08 us takes over 1 us while another wave of the
+//   CU has cold loads outstanding), so a CU that polls for a hand-off while
+//   its own weight loads are in flight waits for all of them.  The workgroups
+//   of each XCD therefore split in two roles that never overlap: 16 "down"
+//   workgroups stream W_down, publish partial dots and end without waiting for
+//   anything; 16 "up" workgroups stream W_up and do every wait after it has
+//   landed.  Both halves issue all their loads at entry, so the whole 13 MB is
+//   in flight at once.
 // * The tiles go straight from memory into LDS (global_load_lds_dwordx4), each
 //   wave instruction fetching 8 whole 128-byte lines.  Measured on MI355X:
 //   loading the same bytes in the matrix cores' operand layout (16 rows x 64
 //   bytes per instruction, half lines) lands the last byte over 1 us later.
-//   Inside LDS the 8 chunks of each line are XOR-swizzled by row, so the
-//   operand reads of 16 rows hit distinct banks.
-// * Every load is issued at entry: W_down first by waves 0-5, then (after a
-//   barrier, so the CU's queue holds W_down ahead of it) W_up by waves 6-7.
-//   A CU serves its vector memory requests in order across waves (measured: a
-//   load that hits L2 in 0.08 us takes over 1 us while another wave of the CU
-//   has cold loads outstanding), so nothing may be issued late.  Barriers are
-//   raw s_barrier with an LDS wait only: the compiler's __syncthreads() also
-//   waits for the LDS-bound loads still in flight.
+//   Inside LDS the chunks of each row are swizzled so that the operand reads
+//   of 16 rows hit distinct banks.  Barriers are raw s_barrier with an LDS
+//   wait only: the compiler's __syncthreads() also waits for LDS-bound loads.
 // * Both projections run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
 //   with tokens as the M dimension.  Each fp32 activation is split exactly into
 //   three bf16 pieces (hi + mid + lo3 == x), so every product is exact and the
 //   result stays fp32-faithful.  Each piece has its own accumulator (three
-//   independent MFMA chains), and the K range is split over two waves.
-// * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40):
-//   its 32 workgroups publish partial dots into the XCD's L2, 20 of them each
-//   reduce two rows (one XCD-local hop) and publish lo device-wide, and every
-//   workgroup gathers all of lo (one device-wide hop).  Hand-off words are 64
-//   bits holding the payload and the launch's generation number, written once
-//   with one store; a consumer polls one sentinel word per producer (its last
-//   store), then reads the data once and re-reads only words whose tag is
-//   still old.  Every workgroup counts its launches in its own slot, so all of
-//   them agree on the generation without host involvement (the launch is
-//   graph-capture safe).  Every wait is bounded.
+//   independent MFMA chains).
+// * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): up
+//   workgroups reduce the 16 partials of 3 rows each through the XCD's L2
+//   (hop 1) and publish lo device-wide; every up workgroup gathers all of lo
+//   (hop 2).  Hand-off words are 64 bits holding the payload and the launch's
+//   generation number, written once with one store; a consumer polls one
+//   sentinel word per producer (its last store), then reads the data once and
+//   re-reads only words whose tag is still old.  Every workgroup counts its
+//   launches in its own slot, so all of them agree on the generation without
+//   host involvement (the launch is graph-capture safe).  Every wait is
+//   bounded.
 #include "hc_internal.h"
 
 // No multiply-add contraction anywhere in this file: a butterfly sum must give
@@ -70,18 +71,52 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr long long kWaitTicks = 5000000;  // 50 ms of the 100 MHz wall clock
-constexpr int kTileRows = 40;               // rows of a weight tile
-constexpr int kTileChunks = kRank / 8;      // 16-byte chunks per tile row (40)
-constexpr int kTileInstr = kTileRows * kTileChunks / 64;  // wave instructions per tile (25)
-constexpr int kUpCols = kWidth / kDecWGs;   // output columns per workgroup (10)
-constexpr int kYRow = kDecCols + 8;         // padded LDS row of an activation plane (bf16)
-constexpr int kLoRow = kRank + 8;           // padded LDS row of a lo plane (bf16)
-constexpr int kStageItems = kDecCols / 4;   // float4 activation items per token (80)
-// scratch layout (in 64-bit words from the base): partial dots, slice sums of
-// squares, lo, then the 32-bit generation counters and the timeout counter
-constexpr size_t kPartWords = (size_t)kDecXcds * kDecPerXcd * kDecRowsPerXcd * kDecMaxT;
-constexpr size_t kSsqWords = (size_t)kDecXcds * kDecPerXcd * kDecMaxT;
-constexpr size_t kLoWords = (size_t)kDecMaxT * kRank;
+constexpr int kTileChunks = 3200;           // 16-byte chunks in either weight tile (51,200 bytes)
+constexpr int kTileInstr = kTileChunks / 64;  // wave instructions per tile (50)
+constexpr int kDnRowChunks = kDecDownCols / 8;  // chunks per W_down tile row (80)
+constexpr int kUpRowChunks = kRank / 8;         // chunks per W_up tile row (40)
+constexpr int kUpRows = 4 * kDecUpCols;         // W_up tile rows (80): row 20 s + r
+constexpr int kStageItems = kDecDownCols / 4;   // float4 activation items per token (160)
+constexpr int kYRow = kDecDownCols + 8;         // padded LDS row of an activation plane (bf16)
+constexpr int kLoRow = kRank + 8;               // padded LDS row of a lo plane (bf16)
+// Scratch layout (in 64-bit words from the base): partial dots, slice sums of
+// squares, lo, then the 32-bit generation counters and the timeout counter.
+// Every producer writes whole 128-byte lines (16 words), padding unused token
+// slots: a line the XCD's L2 holds only in part is filled from memory when it
+// is read, which costs a memory round trip (about 0.5 us while the weights
+// stream) instead of an L2 hit.
+//   part [8 xcd][16 down wg][40 rows][8 tokens]     (two rows per line)
+//   ssq  [8 xcd][16 down wg][16]                    (tokens 0..7, then padding)
+//   lo   [8 replica][8 xcd][16 reducer] blocks of 64 words, the first 32 being
+//        [8 tokens][4 rows] (rows 3 u .. 3 u + 2, padding).  Each reducer writes
+//        one replica per consumer XCD, and the blocks are spread 512 bytes
+//        apart: every line is then read by the 16 up workgroups of one XCD,
+//        spread over many memory channels, instead of by all 128 at once.
+constexpr int kSsqLine = 16;
+constexpr int kLoRows = 4;
+constexpr int kLoBlock = 64;
+constexpr size_t kPartWords = (size_t)kDecXcds * kDecDownPerXcd * kDecRowsPerXcd * kDecMaxT;
+constexpr size_t kSsqWords = (size_t)kDecXcds * kDecDownPerXcd * kSsqLine;
+constexpr size_t kLoWords = (size_t)kDecXcds * kDecXcds * 16 * kLoBlock;
+// word index of (token t, reducer row r) of reducer (xs, us) in replica y
+__host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
+{
+    return ((y * kDecXcds + xs) * 16 + us) * kLoBlock + t * kLoRows + r;
+}
+
+// LDS bytes per role: the weight tile, then the role's planes
+constexpr size_t down_lds(int T)
+{
+    return 16 * kTileChunks + 2 * 3 * T * kYRow + 4 * T * kStageItems + 3 * 64 * 16;
+}
+constexpr size_t up_lds(int T)
+{
+    return 16 * kTileChunks + 2 * 3 * T * kLoRow + 4 * T * kUpRows;
+}
+constexpr size_t lds_bytes(int T)
+{
+    return down_lds(T) > up_lds(T) ? down_lds(T) : up_lds(T);
+}
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
 {
@@ -135,10 +170,6 @@ __device__ __forceinline__ void wait_all_loads()
 }
 // Makes a loaded value "produced here": the compiler may not hoist its use
 // (and the wait for its load) above this point, e.g. above a barrier.
-__device__ __forceinline__ void pin(float& v)
-{
-    asm volatile("" : "+v"(v));
-}
 __device__ __forceinline__ void pin(uint32_t& v)
 {
     asm volatile("" : "+v"(v));
@@ -251,27 +282,36 @@ __device__ __forceinline__ void read_words(const uint64_t* base, int idx, uint32
     }
 }
 
-// Chunk placement inside a tile line: the 8 chunks of a 128-byte line are
-// stored XOR-swizzled by row, so 16 lanes reading the same chunk column of 16
-// consecutive rows hit distinct 16-byte bank groups (with 32 or 64 banks).
+// ---- weight tiles in LDS.  A tile row holds RC chunks of 16 bytes (RC / 8
+// whole 128-byte lines).  The 8 chunks of a line are stored XOR-swizzled by
+// row, and in 80-chunk rows (whose pitch is a multiple of 256 bytes) odd rows
+// also swap neighbouring lines, so 16 lanes reading the same chunk column of
+// 16 consecutive rows hit distinct 16-byte bank groups (with 32 or 64 banks).
 __device__ __forceinline__ int swz(int row)
 {
     return (row & 7) ^ ((row >> 3) & 1);
 }
-// LDS position (in 16-byte chunks) of chunk j (0..39) of tile row `row`.
+template <int RC>
+__device__ __forceinline__ int line_perm(int row, int m)
+{
+    return RC % 16 == 0 ? m ^ (row & 1) : m;
+}
+// LDS position (in chunks) of chunk j of tile row `row`.
+template <int RC>
 __device__ __forceinline__ int tile_pos(int row, int j)
 {
-    return row * kTileChunks + (j & ~7) + ((j & 7) ^ swz(row));
+    return row * RC + 8 * line_perm<RC>(row, j >> 3) + ((j & 7) ^ swz(row));
 }
 // Wave instruction q of a tile load: lane l fills LDS position p = 64 q + l,
-// i.e. (row, line, slot); it fetches that row's chunk 8 line + (slot ^ swz).
-// Eight consecutive lanes fetch one whole 128-byte line.
+// i.e. (row, line, slot); it fetches the chunk that belongs there.  Eight
+// consecutive lanes fetch one whole 128-byte line.
+template <int RC>
 __device__ __forceinline__ void tile_lane(int q, int lane, int& row, int& j)
 {
     const int p = 64 * q + lane;
-    row = p / kTileChunks;
-    const int rem = p - row * kTileChunks;
-    j = (rem & ~7) + ((rem & 7) ^ swz(row));
+    row = p / RC;
+    const int rem = p - row * RC;
+    j = 8 * line_perm<RC>(row, rem >> 3) + ((rem & 7) ^ swz(row));
 }
 // 16 bytes per lane from memory into LDS: lane l's bytes land at
 // lds_wave_base + 16 l (the base must be the same for the whole wave).
@@ -290,19 +330,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16)
 {
     static_assert(T >= 1 && T <= kDecMaxT, "short-window kernel takes 1..8 tokens");
-    static_assert(kTileRows * kTileChunks == 64 * kTileInstr, "tiles are whole wave instructions");
-    static_assert(kDecRowsPerXcd == kTileRows && kUpCols * 4 == kTileRows && kUpCols * kDecWGs == kWidth,
-                  "tiles of 40 rows");
-    static_assert(kDecCols == 8 * kTileChunks && kWidth % kDecCols == 0, "a W_down tile lies in one stream");
-    static_assert(kStageItems * kDecMaxT <= 2 * 384, "two staging passes of waves 0-5");
-    static_assert(kTileRows * kDecMaxT <= 5 * 64, "five mix-operand passes of wave 6");
-    __shared__ __align__(16) uint4 wdt[kTileRows * kTileChunks];  // W_down tile
-    __shared__ __align__(16) uint4 wut[kTileRows * kTileChunks];  // W_up tile, row 10 s + r = column 10 b + r of stream s
-    __shared__ __align__(16) uint16_t ypl[3][T][kYRow];            // y = R' * w_norm, 3 bf16 pieces
-    __shared__ __align__(16) uint16_t lpl[3][T][kLoRow];           // lo, 3 bf16 pieces
-    __shared__ float sspart[T][kStageItems];                      // per-item sums of squares
-    __shared__ __align__(16) f32x4_t comb[3][64];                 // second K half of the accumulators
-    __shared__ float rpl[T][kTileRows];                           // R' of this workgroup's columns
+    static_assert(kDecRowsPerXcd * kDnRowChunks == kTileChunks && kUpRows * kUpRowChunks == kTileChunks,
+                  "both tiles are 3200 chunks");
+    static_assert(kWidth % kDecDownCols == 0, "a W_down tile lies in one stream");
+    static_assert(kDecXcds * kDecRowsPerXcd == kRank && kDecXcds * kDecUpPerXcd * kDecUpCols == kWidth, "cover");
+    static_assert(kStageItems * kDecMaxT <= 3 * kDecThreads && kUpRows * kDecMaxT <= 2 * kDecThreads, "passes");
+    static_assert(kDecReducers <= 16 && kDecRedRows <= 3 && kDecDownPerXcd == 16, "one reducer wave");
+    __shared__ __align__(16) uint4 lds[lds_bytes(T) / 16];
+    uint4* const tile = lds;  // the role's weight tile
 
     DecodeScratch s;
     s.part = scratch;
@@ -317,6 +352,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // MFMA column slot (B / D operand)
     const int g = lane >> 4;  // MFMA k-group (A / B operand) and D row group
+    const int m = lane & 15;  // MFMA A row = token
     // this launch's generation: one more than the launches this workgroup has
     // seen.  Every lane loads the counter (no per-lane branch); the value is
     // used only after the weights have landed.
@@ -324,61 +360,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (threadIdx.x == 0 && __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) != x)
         note_timeout(s.timeouts);  // not on the XCD the hand-offs assume: results invalid
     HC_PROBE(0, threadIdx.x == 0);
-
-    // ---- (1) loads.  Waves 0-5: the W_down tile (rows 40 x + row, columns
-    //      320 i + 8 j ..), then the activations of columns [320 i, 320 i + 320).
-    //      Loads issued before a barrier are unconditional (items past the end
-    //      re-read item 0; a missing pending re-reads R): a conditional load
-    //      makes the compiler merge registers, which waits for every load.
+    // Loads issued before the first wait are unconditional (items past the end
+    // re-read item 0; a missing pending re-reads R): a conditional load makes
+    // the compiler merge registers, which waits for every load.
     const float* Pm = P ? P : R;
-    float4 rv[2], pv[2], wv[2];
-    if (wave < 6) {
-        for (int q = wave; q < kTileInstr; q += 6) {
+
+    if (i < kDecDownPerXcd) {
+        // =========================== down ===========================
+        const int d = i;
+        uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kTileChunks);     // [3][T][kYRow]
+        float* const sspart = reinterpret_cast<float*>(ypl + 3 * T * kYRow);       // [T][160]
+        f32x4_t* const comb = reinterpret_cast<f32x4_t*>(sspart + T * kStageItems);  // [3][64]
+
+        // (1) the W_down tile: rows 40 x + row, columns 640 d + 8 j ..
+        for (int q = wave; q < kTileInstr; q += 8) {
             int row, j;
-            tile_lane(q, lane, row, j);
-            dma16(W_down + (size_t)(kDecRowsPerXcd * x + row) * kD + kDecCols * i + 8 * j, wdt + 64 * q);
+            tile_lane<kDnRowChunks>(q, lane, row, j);
+            dma16(W_down + (size_t)(kDecRowsPerXcd * x + row) * kD + kDecDownCols * d + 8 * j, tile + 64 * q);
         }
+        // the activations of columns [640 d, 640 d + 640)
+        float4 rv[3], pv[3], wv[3];
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int it = threadIdx.x + 384 * pass;
+        for (int pass = 0; pass < 3; ++pass) {
+            const int it = threadIdx.x + kDecThreads * pass;
             const int itc = it < kStageItems * T ? it : 0;
             const int at = itc / kStageItems, f = itc - at * kStageItems;
-            const size_t o = (size_t)at * kD + kDecCols * i + 4 * f;
+            const size_t o = (size_t)at * kD + kDecDownCols * d + 4 * f;
             rv[pass] = *reinterpret_cast<const float4*>(R + o);
             pv[pass] = *reinterpret_cast<const float4*>(Pm + o);
-            wv[pass] = *reinterpret_cast<const float4*>(w_norm + kDecCols * i + 4 * f);
+            wv[pass] = *reinterpret_cast<const float4*>(w_norm + kDecDownCols * d + 4 * f);
         }
-    }
-    wg_barrier();  // B0: every W_down request is queued ahead of the W_up ones
-    // Waves 6-7: the W_up tile (rows s * 2560 + 10 b + r), then (wave 6) R and
-    // pending of this workgroup's 40 columns for the mix.
-    float mr[5], mp[5];
-    if (wave >= 6) {
-        for (int q = wave - 6; q < kTileInstr; q += 2) {
-            int row, j;
-            tile_lane(q, lane, row, j);
-            const int k = (row / kUpCols) * kWidth + kUpCols * b + row % kUpCols;
-            dma16(W_up + (size_t)k * kRank + 8 * j, wut + 64 * q);
-        }
-        if (wave == 6) {
+        // (2) y = R' * w_norm (unscaled: the norm is folded into the
+        //     reduction), its sums of squares, and the exact 3-way split
 #pragma unroll
-            for (int pass = 0; pass < 5; ++pass) {
-                const int it = lane + 64 * pass;  // (token, tile row)
-                const int itc = it < kTileRows * T ? it : 0;
-                const int at = itc / kTileRows, row = itc - at * kTileRows;
-                const size_t o = (size_t)at * kD + (row / kUpCols) * kWidth + kUpCols * b + row % kUpCols;
-                mr[pass] = R[o];
-                mp[pass] = Pm[o];
-            }
-        }
-    }
-
-    // ---- (2) waves 0-5 stage y = R' * w_norm (unscaled: the norm is folded
-    //      into the reduction), its sums of squares, and the exact 3-way split.
-    if (wave < 6) {
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int it = threadIdx.x + 384 * pass;
+        for (int pass = 0; pass < 3; ++pass) {
+            const int it = threadIdx.x + kDecThreads * pass;
             if (it < kStageItems * T) {
                 const int at = it / kStageItems, f = it - at * kStageItems;
                 const float r[4] = {P ? rv[pass].x + pv[pass].x : rv[pass].x, P ? rv[pass].y + pv[pass].y : rv[pass].y,
@@ -391,147 +407,202 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     ss += r[e] * r[e];
                     split3(r[e] * w[e], hi[e], mi[e], lo[e]);
                 }
-                sspart[at][f] = ss;
+                sspart[at * kStageItems + f] = ss;
                 const int col = 4 * f;
-                *reinterpret_cast<uint2*>(&ypl[0][at][col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-                *reinterpret_cast<uint2*>(&ypl[1][at][col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-                *reinterpret_cast<uint2*>(&ypl[2][at][col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                *reinterpret_cast<uint2*>(&ypl[(0 * T + at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+                *reinterpret_cast<uint2*>(&ypl[(1 * T + at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
+                *reinterpret_cast<uint2*>(&ypl[(2 * T + at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
             }
         }
-        wait_all_loads();  // this wave's part of the W_down tile is in LDS
-    }
-    wg_barrier();  // B1: activations staged, W_down tile complete
-    HC_PROBE(1, threadIdx.x == 0);
+        wait_all_loads();  // this wave's part of the tile is in LDS
+        wg_barrier();      // B1: activations staged, W_down tile complete
+        HC_PROBE(1, threadIdx.x == 0);
 
-    // ---- (3) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
-    //      tile (block 2: rows 32..39, its upper 8 slots repeat them) over
-    //      K steps 5 (w / 3) .. +4 of 32 columns.
-    f32x4_t dacc = {0.f, 0.f, 0.f, 0.f};
-    if (wave < 6) {
-        const int nb = wave % 3, kh = wave / 3;
-        const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
-        const int m = lane & 15;  // A row = token
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+        // (3) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
+        //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over
+        //     K steps 10 (w / 3) .. +9 of 32 columns
+        f32x4_t dacc = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 6) {
+            const int nb = wave % 3, kh = wave / 3;
+            const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
+            // all operands first (one LDS latency, not ten); A rows >= T
+            // repeat token T - 1: they only feed D rows >= T, never stored
+            const int mc = m < T ? m : T - 1;
+            uint4 wb[10], ah[10], am[10], al[10];
 #pragma unroll
-        for (int qq = 0; qq < 5; ++qq) {
-            const int q = 5 * kh + qq;
-            const uint4 wb = wdt[tile_pos(row, 4 * q + g)];
-            const int col = 32 * q + 8 * g;
-            uint4 ah = make_uint4(0, 0, 0, 0), am = ah, al = ah;
-            if (m < T) {
-                ah = *reinterpret_cast<const uint4*>(&ypl[0][m][col]);
-                am = *reinterpret_cast<const uint4*>(&ypl[1][m][col]);
-                al = *reinterpret_cast<const uint4*>(&ypl[2][m][col]);
+            for (int qq = 0; qq < 10; ++qq) {
+                const int q = 10 * kh + qq;
+                const int col = 32 * q + 8 * g;
+                wb[qq] = tile[tile_pos<kDnRowChunks>(row, 4 * q + g)];
+                ah[qq] = *reinterpret_cast<const uint4*>(&ypl[(0 * T + mc) * kYRow + col]);
+                am[qq] = *reinterpret_cast<const uint4*>(&ypl[(1 * T + mc) * kYRow + col]);
+                al[qq] = *reinterpret_cast<const uint4*>(&ypl[(2 * T + mc) * kYRow + col]);
             }
-            a0 = mfma16(ah, wb, a0);
-            a1 = mfma16(am, wb, a1);
-            a2 = mfma16(al, wb, a2);
+            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+#pragma unroll
+            for (int qq = 0; qq < 10; ++qq) {
+                a0 = mfma16(ah[qq], wb[qq], a0);
+                a1 = mfma16(am[qq], wb[qq], a1);
+                a2 = mfma16(al[qq], wb[qq], a2);
+            }
+            dacc = a0 + (a1 + a2);
+            if (kh == 1)
+                comb[nb * 64 + lane] = dacc;
         }
-        dacc = a0 + (a1 + a2);
-        if (kh == 1)
-            comb[nb][lane] = dacc;
+        HC_PROBE(2, threadIdx.x == 0);
+        wg_barrier();  // Bc1: second K halves in LDS
+        pin(seen);
+        const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
+
+        if (wave < 3) {
+            // (4) partial dots of rows 16 nb + n, tokens 4 g + e, into the XCD's L2
+            //     (all 8 token slots, whole lines; slots >= T hold values nobody reads)
+            dacc = dacc + comb[wave * 64 + lane];
+            const int row = 16 * wave + n;
+            if (row < kDecRowsPerXcd && g < 2) {
+                uint64_t* dst = s.part + (((size_t)x * kDecDownPerXcd + d) * kDecRowsPerXcd + row) * kDecMaxT + 4 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    st_word_xcd(dst + e, tag_f32(dacc[e], gen));
+            }
+        } else if (wave == 3) {
+            // (4') the slice's sum of squares per token: lane 8 t + p sums 20
+            //      of token t's 160 item sums, then the 8 lanes combine theirs
+            const int tt = lane >> 3, p = lane & 7;
+            float ss = 0.f;
+            if (tt < T) {
+#pragma unroll
+                for (int f = 0; f < 20; ++f)
+                    ss += sspart[tt * kStageItems + 20 * p + f];
+            }
+            ss = sum8(ss);
+            if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
+                st_word_xcd(&s.ssq[((size_t)x * kDecDownPerXcd + d) * kSsqLine + 8 * p + tt], tag_f32(p == 0 ? ss : 0.f, gen));
+        }
+        HC_PROBE(3, threadIdx.x == 0);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&s.gen[b], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
-    HC_PROBE(2, threadIdx.x == 0);
-    wg_barrier();  // Bc1: second K halves in LDS
+
+    // ============================= up =============================
+    const int u = i - kDecDownPerXcd;
+    const int c0 = kDecUpCols * (kDecUpPerXcd * x + u);  // first output column
+    uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kTileChunks);  // [3][T][kLoRow]
+    float* const rpl = reinterpret_cast<float*>(lpl + 3 * T * kLoRow);      // [T][80]: R' of tile row 20 s + r
+
+    // (0) a reducer first touches (plain loads, which keep the lines in this
+    //     XCD's L2) the lines it will poll: the 16 producers' partial rows
+    //     3 u .. 3 u + 2 and their sums of squares.  Polls then hit L2 and see
+    //     a producer's store as soon as it lands, instead of each round
+    //     fetching the line from memory.  (Only lines written inside this XCD
+    //     are touched this way.)
+    if (wave == 0 && u < kDecReducers) {
+        const int src = lane & 15, k = lane >> 4;  // k 0..2: partial lines, 3: sums of squares
+        const int rowl = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
+        const uint64_t* line = k < 3 ? s.part + (((size_t)x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowl) * kDecMaxT
+                                     : s.ssq + ((size_t)x * kDecDownPerXcd + src) * kSsqLine;
+        const uint32_t touched = *reinterpret_cast<const volatile uint32_t*>(line);
+        asm volatile("" ::"v"(touched));
+    }
+    // (1) the W_up tile: rows s * 2560 + c0 + r (tile row 20 s + r)
+    for (int q = wave; q < kTileInstr; q += 8) {
+        int row, j;
+        tile_lane<kUpRowChunks>(q, lane, row, j);
+        const int k = (row / kDecUpCols) * kWidth + c0 + row % kDecUpCols;
+        dma16(W_up + (size_t)k * kRank + 8 * j, tile + 64 * q);
+    }
+    // R and pending of the same 80 (stream, column) pairs, for the mix
+    float mr[2], mp[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int it = threadIdx.x + kDecThreads * pass;
+        const int itc = it < kUpRows * T ? it : 0;
+        const int at = itc / kUpRows, row = itc - at * kUpRows;
+        const size_t o = (size_t)at * kD + (row / kDecUpCols) * kWidth + c0 + row % kDecUpCols;
+        mr[pass] = R[o];
+        mp[pass] = Pm[o];
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int it = threadIdx.x + kDecThreads * pass;
+        if (it < kUpRows * T)
+            rpl[it] = P ? mr[pass] + mp[pass] : mr[pass];  // it = 80 t + row
+    }
+    wait_all_loads();  // every load of this CU has landed: from here on, hand-off loads run at cache latency
+    wg_barrier();      // B1
+    HC_PROBE(1, threadIdx.x == 0);
     pin(seen);
     const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
 
-    if (wave < 3) {
-        // ---- (4) partial dots of rows 16 nb + n, tokens 4 g + e, into the XCD's L2
-        dacc = dacc + comb[wave][lane];
-        const int row = 16 * wave + n;
-        if (row < kTileRows) {
-            uint64_t* dst = s.part + (((size_t)x * kDecPerXcd + i) * kTileRows + row) * kDecMaxT + 4 * g;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * g + e < T)
-                    st_word_xcd(dst + e, tag_f32(dacc[e], gen));
-        }
-    } else if (wave == 3) {
-        // ---- (4') the slice's sum of squares per token: lane 8 t + p sums 10
-        //      of token t's 80 item sums, then the 8 lanes combine theirs
-        const int tt = lane >> 3, p = lane & 7;
-        float ss = 0.f;
-        if (tt < T) {
-#pragma unroll
-            for (int f = 0; f < 10; ++f)
-                ss += sspart[tt][10 * p + f];
-        }
-        ss = sum8(ss);
-        if (tt < T && p == 0)
-            st_word_xcd(&s.ssq[((size_t)x * kDecPerXcd + i) * kDecMaxT + tt], tag_f32(ss, gen));
-    }
-    HC_PROBE(3, threadIdx.x == 0);
-
-    if (wave == 7 && i < kDecReducers) {
-        // ---- (5) hop 1: rows 40 x + 2 i + r (r = lane / 32) over the XCD's 32
-        //      partials (lane % 32 = source workgroup), each stream's rs from
-        //      its 8 slices' sums of squares, lo published device-wide.
-        const int r = lane >> 5, src = lane & 31;
-        const int row = 2 * i + r;
-        const int pidx = ((x * kDecPerXcd + src) * kTileRows + row) * kDecMaxT;
-        const int sidx = (x * kDecPerXcd + src) * kDecMaxT;
-        const long long t0 = wall_clock64();
-        const bool live = wait_sentinels(s.part, pidx + T - 1, s.ssq, sidx + T - 1, gen, t0, lane, s.timeouts, 0);
-        float v[T], q[T];
-        read_words<T>(s.part, pidx, gen, live, t0, lane, v, s.timeouts, 0);
-        read_words<T>(s.ssq, sidx, gen, live, t0, lane, q, s.timeouts, 1);
-        HC_PROBE(12, lane == 0);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            // lanes 8 s .. 8 s + 7 (of each half) hold the slices of stream s
-            const float ss = sum8(q[t]);
-            const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
-            const float y = sum8(v[t]) * rs;
-            const float y01 = y + dpp<0x128>(y);         // row_ror:8: streams (0 + 1), (2 + 3)
-            const float lo = y01 + __shfl_xor(y01, 16);  // (s0 + s1) + (s2 + s3)
-            if (src == t)
-                st_word(&s.lo[(size_t)t * kRank + kDecRowsPerXcd * x + row], tag_f32(lo, gen));
-        }
-        HC_PROBE(13, lane == 0);
-    }
-
-    if (wave == 6) {
-        // ---- (6') R' = R + pending of this workgroup's columns, for the mix
-#pragma unroll
-        for (int pass = 0; pass < 5; ++pass) {
-            const int it = lane + 64 * pass;
-            pin(mr[pass]);
-            pin(mp[pass]);
-            if (it < kTileRows * T) {
-                const int at = it / kTileRows, row = it - at * kTileRows;
-                rpl[at][row] = P ? mr[pass] + mp[pass] : mr[pass];
-            }
-        }
-    }
-    wg_barrier();  // Bh: this workgroup's hop 1 is done before any hop-2 load
-                   // (a CU serves loads in order: a hop-2 load behind which a
-                   // hop-1 load waits would delay every consumer of this row)
     if (wave == 0) {
-        // ---- (6) hop 2, first: wait for this XCD's 20 reducers (their odd
-        //      row, last token).  The other XCDs run in step with this one, so
-        //      their lo is then due too; polling only local words keeps the
-        //      device-wide traffic to one bulk read per workgroup.
+        if (u < kDecReducers) {
+            // (5) hop 1: rows 3 u + r (r = lane / 16 < 3) over the XCD's 16
+            //     partials (lane % 16 = down workgroup), each stream's rs from
+            //     its 4 slices' sums of squares; lo published device-wide
+            const int r = lane >> 4, src = lane & 15;
+            const int row = kDecRedRows * u + r;
+            const bool valid = r < kDecRedRows && row < kDecRowsPerXcd;
+            const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
+            const int pidx = ((x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowc) * kDecMaxT;
+            const int sidx = (x * kDecDownPerXcd + src) * kSsqLine;
+            const long long t0 = wall_clock64();
+            const bool live = wait_sentinels(s.part, valid ? pidx + T - 1 : -1, s.ssq, sidx + T - 1, gen, t0, lane,
+                                             s.timeouts, 0);
+            float v[T], q[T];
+            read_words<T>(s.part, pidx, gen, live, t0, lane, v, s.timeouts, 0);
+            read_words<T>(s.ssq, sidx, gen, live, t0, lane, q, s.timeouts, 1);
+            HC_PROBE(12, lane == 0);
+            float mine = 0.f;  // lo of row 3 u + r, token `src`
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
+                const float ss = sum4(q[t]);
+                const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+                const float y = sum4(v[t]) * rs;
+                const float y01 = y + dpp<0x141>(y);      // row_half_mirror: (s0 + s1), (s2 + s3)
+                const float lo = y01 + dpp<0x140>(y01);   // row_mirror: (s0 + s1) + (s2 + s3)
+                if (src == t)
+                    mine = lo;
+            }
+            // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
+            // this reducer, 0 in the padding
+            const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
+#pragma unroll
+            for (int y = 0; y < kDecXcds; ++y)
+                if (src < kDecMaxT)
+                    st_word(&s.lo[lo_word(y, x, u, src, r)], word);
+            HC_PROBE(13, lane == 0);
+        }
+        // (6) hop 2, first: wait for this XCD's reducers (the last row of
+        //     each, last token).  The other XCDs run in step with this one, so
+        //     their lo is then due too; polling only local words keeps the
+        //     device-wide traffic to one read per workgroup.
         const long long t0 = wall_clock64();
-        const int sent = lane < kDecReducers ? (T - 1) * kRank + kDecRowsPerXcd * x + 2 * lane + 1 : -1;
+        const int sent = lane < kDecReducers ? lo_word(x, x, lane, T - 1, 2) : -1;
         HC_PROBE(15, lane == 0);
         wait_sentinels(s.lo, sent, s.lo, -1, gen, t0, lane, s.timeouts, 2);  // (a timeout is counted; the reads below are bounded too)
         HC_PROBE(14, lane == 0);
     }
     wg_barrier();  // Bs
     if (wave < 4) {
-        // ---- (6) hop 2, then: wave w reads lo rows [80 w, 80 w + 80) (XCDs
-        //      2 w, 2 w + 1), two rows per slot, re-reading words whose tag is
-        //      still old, and stages their 3 bf16 pieces
-        constexpr int NS = (40 * T + 63) / 64;  // slots per lane
-        const int rbase = 80 * wave;
+        // (6) hop 2, then: wave w reads the reducers of XCDs 2 w and 2 w + 1
+        //     (slot = reducer, token, pair of rows), re-reading words whose
+        //     tag is still old, and stages the 3 bf16 pieces of each value
+        constexpr int NS = (2 * kDecReducers * T * 2 + 63) / 64;  // slots per lane
         const long long t0 = wall_clock64();
         uint4 lw[NS];
         bool done[NS];
+        int widx[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
+            const int sl = lane + 64 * k;
+            const int pair = sl & 1, rest = sl >> 1;
+            const int tt = rest % T, red = rest / T;  // red: 0 .. 27
+            const int xs = 2 * wave + red / kDecReducers, us = red % kDecReducers;
+            widx[k] = lo_word(x, xs, us, tt, 2 * pair);
             lw[k] = make_uint4(0, 0, 0, 0);
-            done[k] = lane + 64 * k >= 40 * T;
+            done[k] = sl >= 2 * kDecReducers * T * 2;
         }
         [[maybe_unused]] int rounds = 0;
         while (true) {
@@ -539,9 +610,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             bool all = true;
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
-                const int sl = lane + 64 * k;
                 if (!done[k]) {
-                    lw[k] = ld_words2(s.lo, (sl / 40) * kRank + rbase + 2 * (sl % 40));
+                    lw[k] = ld_words2(s.lo, widx[k]);
                     done[k] = lw[k].y == gen && lw[k].w == gen;
                 }
                 all = all && done[k];
@@ -560,69 +630,61 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int sl = lane + 64 * k;
-            if (sl < 40 * T) {
-                const int tt = sl / 40;
-                const int jr = rbase + 2 * (sl % 40);
-                uint32_t h0, m0, l0, h1, m1, l1;
-                split3(__uint_as_float(lw[k].x), h0, m0, l0);
-                split3(__uint_as_float(lw[k].z), h1, m1, l1);
-                *reinterpret_cast<uint32_t*>(&lpl[0][tt][jr]) = h0 | (h1 << 16);
-                *reinterpret_cast<uint32_t*>(&lpl[1][tt][jr]) = m0 | (m1 << 16);
-                *reinterpret_cast<uint32_t*>(&lpl[2][tt][jr]) = l0 | (l1 << 16);
+            if (sl < 2 * kDecReducers * T * 2) {
+                const int pair = sl & 1, rest = sl >> 1;
+                const int tt = rest % T, red = rest / T;
+                const int xs = 2 * wave + red / kDecReducers, us = red % kDecReducers;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int rr = 2 * pair + h;               // row of the reducer, 0..3
+                    const int rowl = kDecRedRows * us + rr;    // row of the XCD, 0..39
+                    if (rr < kDecRedRows && rowl < kDecRowsPerXcd) {
+                        const int jr = kDecRowsPerXcd * xs + rowl;
+                        uint32_t hb, mb, lb;
+                        split3(__uint_as_float(h ? lw[k].z : lw[k].x), hb, mb, lb);
+                        lpl[(0 * T + tt) * kLoRow + jr] = (uint16_t)hb;
+                        lpl[(1 * T + tt) * kLoRow + jr] = (uint16_t)mb;
+                        lpl[(2 * T + tt) * kLoRow + jr] = (uint16_t)lb;
+                    }
+                }
             }
         }
         HC_PROBE(7, wave == 0 && lane == 0);
     }
-    if (wave >= 6)
-        wait_all_loads();  // the W_up tile is in LDS
-    HC_PROBE(6, wave == 6 && lane == 0);
-    wg_barrier();  // B2: lo staged, W_up tile complete
+    wg_barrier();  // B2: lo staged
     HC_PROBE(8, threadIdx.x == 0);
 
-    // ---- (7) up projection: wave w < 6 takes output columns 4 (w % 3) .. +3
-    //      of this workgroup (block 2: columns 8, 9; its slots for the block's
-    //      columns 2, 3 repeat them and store nothing) over K steps
-    //      5 (w / 3) .. +4; slot n = 4 (column) + stream.
-    const int u = wave % 3;
-    const int cc = n >> 2, st = n & 3;
-    const bool owner = 4 * u + cc < kUpCols;
-    const int cr = owner ? 4 * u + cc : 4 * u + (cc & 1);  // column inside the workgroup's 10
-    f32x4_t uacc = {0.f, 0.f, 0.f, 0.f};
-    if (wave < 6) {
-        const int kh = wave / 3;
-        const int row = st * kUpCols + cr;
-        const int m = lane & 15;
+    if (wave < kDecUpCols / 4) {
+        // (7) up projection: wave w < 5 takes output columns c0 + 4 w .. +3
+        //     (slot n = 4 column + stream), all 10 K steps; gated = up
+        //     (identity epilogue); then the mix of the 4 streams of a column
+        const int cc = n >> 2, st = n & 3;
+        const int row = st * kDecUpCols + 4 * wave + cc;
+        const int mc = m < T ? m : T - 1;  // (rows >= T feed only D rows >= T)
+        uint4 wb[10], ah[10], am[10], al[10];
+#pragma unroll
+        for (int q = 0; q < 10; ++q) {
+            const int jc = 32 * q + 8 * g;
+            wb[q] = tile[tile_pos<kUpRowChunks>(row, 4 * q + g)];
+            ah[q] = *reinterpret_cast<const uint4*>(&lpl[(0 * T + mc) * kLoRow + jc]);
+            am[q] = *reinterpret_cast<const uint4*>(&lpl[(1 * T + mc) * kLoRow + jc]);
+            al[q] = *reinterpret_cast<const uint4*>(&lpl[(2 * T + mc) * kLoRow + jc]);
+        }
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
 #pragma unroll
-        for (int qq = 0; qq < 5; ++qq) {
-            const int q = 5 * kh + qq;
-            const uint4 wb = wut[tile_pos(row, 4 * q + g)];
-            const int jc = 32 * q + 8 * g;
-            uint4 ah = make_uint4(0, 0, 0, 0), am = ah, al = ah;
-            if (m < T) {
-                ah = *reinterpret_cast<const uint4*>(&lpl[0][m][jc]);
-                am = *reinterpret_cast<const uint4*>(&lpl[1][m][jc]);
-                al = *reinterpret_cast<const uint4*>(&lpl[2][m][jc]);
-            }
-            a0 = mfma16(ah, wb, a0);
-            a1 = mfma16(am, wb, a1);
-            a2 = mfma16(al, wb, a2);
+        for (int q = 0; q < 10; ++q) {
+            a0 = mfma16(ah[q], wb[q], a0);
+            a1 = mfma16(am[q], wb[q], a1);
+            a2 = mfma16(al[q], wb[q], a2);
         }
-        uacc = a0 + (a1 + a2);
-        if (kh == 1)
-            comb[u][lane] = uacc;
-    }
-    wg_barrier();  // Bc2
-    if (wave < 3) {
-        // gated = up (identity epilogue); mix the 4 streams of the column
-        uacc = uacc + comb[u][lane];
-        const int c = kUpCols * b + cr;
+        const f32x4_t uacc = a0 + (a1 + a2);
+        const int c = c0 + 4 * wave + cc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tt = 4 * g + e;
-            const float rp = rpl[tt < T ? tt : 0][st * kUpCols + cr];
+            const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
             const float mixed = sum4(uacc[e] * rp);  // (s0 + s1) + (s2 + s3)
-            if (st == 0 && owner && tt < T) {
+            if (st == 0 && tt < T) {
                 const size_t o = (size_t)tt * kWidth + c;
                 out_mixed[o] = mixed;
                 out_bf16[o] = __builtin_bit_cast(uint16_t, (__bf16)mixed);

@@ -17,31 +17,35 @@ constexpr float kEps = 1e-6f;
 // Short-window path (T <= kDecMaxT): one launch of kDecWGs workgroups, one
 // per CU, each of 8 waves.  Workgroup b runs on XCD x = b % 8 (the dispatcher
 // deals workgroups to the 8 XCDs round robin; the kernel checks it); i = b / 8.
-//   down: XCD x owns lo rows [40 x, 40 x + 40); workgroup (x, i) computes
-//     their partial dots over columns [320 i, 320 i + 320) (inside stream
-//     i / 8) with that slice's sum of squares;
-//   hop 1 (inside the XCD, through its L2): workgroups i < 20 each reduce two
-//     rows over the XCD's 32 partials, applying each stream's rs, and publish
-//     lo device-wide;
-//   hop 2 (across XCDs): every workgroup gathers all 320 values of lo;
-//   up: workgroup b owns output columns [10 b, 10 b + 10) (all 4 streams of
-//     each), then the stream mix.
-// Weight tiles (40 rows x 320 bf16 each) are loaded straight into LDS as whole
-// cache lines.  Hand-off words are 64 bits: payload plus the launch's
-// generation number, written once with one store and polled by the consumer.
+// Each XCD's 32 workgroups split into two roles, so that no CU polls while
+// its own weight loads are in flight:
+//   down (i < 16, d = i): W_down rows [40 x, 40 x + 40) x columns
+//     [640 d, 640 d + 640) (inside stream d / 4); the partial dots and the
+//     slice's sum of squares go into the XCD's L2; then the workgroup ends;
+//   up (i >= 16, u = i - 16): W_up rows of output columns
+//     [20 (16 x + u), +20), all 4 streams.  Once they have landed, up
+//     workgroups u < 14 each reduce 3 rows of the XCD's 40 (hop 1, inside the
+//     XCD) and publish lo device-wide; every up workgroup then gathers all of
+//     lo (hop 2), runs the up projection and the stream mix.
+// Weight tiles are loaded straight into LDS as whole cache lines.  Hand-off
+// words are 64 bits: payload plus the launch's generation number, written
+// once with one store and polled by the consumer.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 8;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;
-constexpr int kDecPerXcd = kDecWGs / kDecXcds;     // 32 workgroups per XCD
-constexpr int kDecRowsPerXcd = kRank / kDecXcds;   // 40 lo rows per XCD
-constexpr int kDecCols = kD / kDecPerXcd;          // 320 W_down columns per workgroup
-constexpr int kDecReducers = kDecRowsPerXcd / 2;   // 20 workgroups per XCD reduce 2 rows each
+constexpr int kDecDownPerXcd = 16;                               // down workgroups per XCD
+constexpr int kDecUpPerXcd = 16;                                 // up workgroups per XCD
+constexpr int kDecRowsPerXcd = kRank / kDecXcds;                 // 40 lo rows per XCD
+constexpr int kDecDownCols = kD / kDecDownPerXcd;                // 640 W_down columns per down workgroup
+constexpr int kDecUpCols = kWidth / (kDecXcds * kDecUpPerXcd);   // 20 output columns per up workgroup
+constexpr int kDecRedRows = 3;                                   // lo rows each reducing up workgroup reduces
+constexpr int kDecReducers = (kDecRowsPerXcd + kDecRedRows - 1) / kDecRedRows;  // 14 per XCD
 
 struct DecodeScratch {
-    uint64_t* part;      // [8 xcd][32 wg][40 rows][kDecMaxT]: partial dots (XCD-local)
-    uint64_t* ssq;       // [8 xcd][32 wg][kDecMaxT]: column-slice sums of squares (XCD-local)
+    uint64_t* part;      // [8 xcd][16 down wg][40 rows][kDecMaxT]: partial dots (XCD-local)
+    uint64_t* ssq;       // [8 xcd][16 down wg][kDecMaxT]: column-slice sums of squares (XCD-local)
     uint64_t* lo;        // [kDecMaxT][kRank]: lo (device-wide)
     uint32_t* gen;       // [kDecWGs]: launches completed by each workgroup
     uint32_t* timeouts;  // [1]: expired bounded waits and misplaced workgroups
