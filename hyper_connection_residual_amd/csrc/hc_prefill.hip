@@ -5,28 +5,45 @@
 // finer" with the norm folded into the down projection ("#2488 sycl/A770",
 // Summary item 4) and the up projection fused with gr_mix_r as in "#1370
 // prefill: ... gr_mix_r as its epilogue", "What it does": gated (T x 10240
-// fp32) never leaves registers and LDS.  Three launches per chunk of up to
-// 4096 tokens:
+// fp32) never leaves registers.  Three launches per chunk of up to 4096 tokens:
 //
 //   P1 down:  part[sig][t][j] = sum_{k in split sig} W_down[j][k] * (R'[t][k] *
-//             w_norm[k]) and ssq[sig][t] = sum_{k in sig} R'[t][k]^2, where a
-//             split is one stream (or half of one).  Tile: 64 tokens x 320 rows,
-//             K streamed 32 columns at a time through double-buffered LDS.
-//   P2 lo:    rs[t][s] = 1/sqrt(sum_{sig in s} ssq / 2560 + eps) and lo[t][j] =
-//             sum_s rs[t][s] * sum_{sig in s} part[sig][t][j], stored as three
-//             bf16 planes (an exact split of the fp32 value).
-//   P3 up+mix: a tile of 128 tokens x 32 output columns x 4 streams: the up
+//             w_norm[k]) and ssq[sig][t] = sum_{k in sig} R'[t][k]^2, where the
+//             8 splits are the halves of the 4 streams (1280 columns each).
+//   P2 lo:    rs[t][s] = 1/sqrt(sum of stream s's two ssq / 2560 + eps) and
+//             lo[t][j] = sum_s rs[t][s] * (stream s's two partials), stored as
+//             three bf16 planes (an exact split of the fp32 value) in the
+//             tiled layout P3 copies into LDS verbatim.
+//   P3 up+mix: a tile of 64 tokens x 64 output columns x 4 streams: the up
 //             projection (K = 320) on the matrix cores, then the mix of the 4
-//             streams with R' and the bf16 / fp16 images, written coalesced
-//             after a transpose through LDS.
+//             streams with R' and the bf16 / fp16 images, all in registers.
 //
-// gfx950 choices: bf16 v_mfma_f32_16x16x32_bf16 with every fp32 activation
-// split exactly into three bf16 pieces (so products are exact and results stay
-// fp32-faithful); workgroups sharing a W_down slice (P1) or a token tile (P3)
-// are dealt to the same XCD so the shared operand is served from that XCD's
-// L2; the chunk size keeps a chunk's R (+ pending) within the 256 MB Infinity
-// Cache for its second read in P3.
+// gfx950 design:
+// * Both matrix kernels run bf16 v_mfma_f32_16x16x32_bf16 with every fp32
+//   activation split exactly into three bf16 pieces (hi + mid + lo3 == x), so
+//   each product is exact and the result stays fp32-faithful.
+// * Weight operands (and P3's lo planes) go from memory straight into LDS
+//   (global_load_lds_dwordx4, 16 bytes a lane) through a two-stage ring, one K
+//   step of 32 ahead of the matrix cores.  LDS is read with inline-asm
+//   ds_read_b128 and every wait is explicit: the compiler, seeing an LDS read
+//   that may alias a load still landing in LDS, would wait for ALL loads in
+//   flight (vmcnt(0)) and serialise the ring.
+// * Inside LDS a K step of a tile is a "panel": one row per matrix row, four
+//   16-byte chunks per row, chunk c of row r stored at slot 4 r + (c ^ ((r >>
+//   2) & 3)).  The 16 lanes that read one chunk column of 16 consecutive rows
+//   then hit 16 distinct 16-byte bank groups.
+// * Both kernels use 4 waves and 56-64 KB of LDS, so two workgroups share a
+//   CU: one's epilogue (memory bound) overlaps the other's matrix work.
+// * XCD-aware grids (workgroup b runs on XCD b % 8): P1's XCD x owns split x,
+//   so its 820 KB W_down slice stays in that XCD's L2; P3's XCD x owns 5 of
+//   the 40 column groups (W_up slices, 820 KB) and walks the token tiles, the 5
+//   workgroups of one tile being dispatched together so its lo planes are read
+//   once per XCD.
+// * The chunk keeps a chunk's R (+ pending) within the 256 MB Infinity Cache
+//   for its second read in P3.
 #include "hc_internal.h"
+
+#include <type_traits>
 
 #pragma clang fp contract(off)
 
@@ -35,8 +52,9 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
+__device__ __forceinline__ f32x4_t mfma16(u32x4 a, u32x4 b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -54,358 +72,528 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
     lo3 = __float_as_uint(r2) >> 16;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
+// ---- LDS access with explicit waits ----------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+    return (uint32_t)(uintptr_t)p;  // the low 32 bits of a shared-aperture address are the LDS offset
 }
-__device__ __forceinline__ float sum4(float v)
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr)
 {
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
     return v;
 }
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16_off(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+    return v;
+}
+// Waits for every LDS read of this wave; the values in `v` are then "produced
+// here", so no use of them moves above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&v)[N])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : "+v"(v[i]));
+}
+// No memory access moves across this point.
+__device__ __forceinline__ void order()
+{
+    asm volatile("" ::: "memory");
+}
+// Waits until at most VM of this wave's memory loads are in flight and its
+// LDS accesses are done, then the workgroup barrier.
+template <int VM>
+__device__ __forceinline__ void ring_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+// 16 bytes per lane from memory into LDS: lane l's bytes land at
+// lds_wave_base + 16 l (the base must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* g, uint4* lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+}
 
-constexpr int kP1Tok = 64;               // P1 token tile
-constexpr int kP1Row = 32 + 8;           // padded LDS row (bf16) of a 32-column step
-constexpr int kP3Tok = 128;              // P3 token tile
-constexpr int kP3Cols = 32;              // P3 output columns per tile
-constexpr int kP3ColTiles = kWidth / kP3Cols;  // 80
+// Slot (in 16-byte chunks) of chunk c (0..3) of row r in a panel.
+__host__ __device__ constexpr int panel_slot(int r, int c)
+{
+    return 4 * r + (c ^ ((r >> 2) & 3));
+}
+
+constexpr int kTok = 64;                       // token tile of both matrix kernels
+constexpr int kKs = 32;                        // K step: one MFMA depth
+constexpr int kUpSteps = kRank / kKs;          // 10
+constexpr int kUpCols = 64;                    // P3 output columns per tile
+constexpr int kUpGroups = kWidth / kUpCols;    // 40 column groups
+constexpr int kGroupsPerXcd = kUpGroups / 8;   // 5
+constexpr int kPlaneChunks = kTok * 4;         // one plane panel of a token tile: 256 chunks (4 KB)
+constexpr int kLoBlock = 3 * kPlaneChunks;     // the three planes of one (tile, K step): 12 KB
 
 // ---------------------------------------------------------------------------
-// P1: down projection partials and sums of squares.
+// P1: down projection partials and sums of squares.  Workgroup b: split
+// b % S of width 10240 / S (stream halves or quarters; with S = 8 the split is
+// the XCD's, with S = 16 each XCD owns two), token tile b / S of 128 tokens.
+// Wave w owns tokens 16 w .. 16 w + 15 of the tile and computes all 320 rows
+// for them: MFMA A = W_down rows (20 blocks of 16), B = that wave's y = R' *
+// w_norm, split in registers into its three bf16 pieces (each wave converts
+// only its own tokens, so no y panel is shared through LDS).
+// Everything reaches LDS by direct loads: the W_down panel of a step one step
+// ahead (2 slots), raw R and pending two steps ahead (3 slots), and the
+// split's w_norm once.  No loaded value lives in registers across a step.
+// Raw rows are 32 floats (8 chunks of 16 bytes); chunk c of row r sits at slot
+// c ^ swz(r) of its 128-byte line, so 16 lanes reading one chunk of 16 rows
+// hit distinct bank groups.
+// ---------------------------------------------------------------------------
+constexpr int kDnTok = 128;
+constexpr int kDnWaves = 8;
+constexpr int kDnWChunks = kRank * 4;           // W_down panel: 1280 chunks (20 KB)
+constexpr int kDnRawChunks = kDnTok * 8;        // raw R (or pending) of a step: 1024 chunks (16 KB)
+
+__device__ __forceinline__ int swz8(int row)
+{
+    return (row & 7) ^ ((row >> 3) & 1);
+}
+
+template <int S, bool HAS_P>
+__global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float* __restrict__ R,
+                                                              const float* __restrict__ P,
+                                                              const float* __restrict__ w_norm,
+                                                              const uint16_t* __restrict__ W_down,
+                                                              float* __restrict__ part, float* __restrict__ ssq)
+{
+    constexpr int SW = kD / S;              // columns of a split
+    constexpr int NS = SW / kKs;            // K steps
+    constexpr int kRawSlots = 3;
+    constexpr int kRawSet = (HAS_P ? 2 : 1) * kDnRawChunks;
+    // LDS (chunks): 2 W_down slots, 3 raw slots (R, then pending), w_norm
+    constexpr int kWOff = 0;
+    constexpr int kRawOff = 2 * kDnWChunks;
+    constexpr int kNormOff = kRawOff + kRawSlots * kRawSet;
+    constexpr int kLdsChunks = kNormOff + SW / 4;
+    // raw-load wave instructions per step and wave (16 per array, 8 waves)
+    constexpr int kRawLoads = (HAS_P ? 2 : 1) * (kDnRawChunks / 64) / kDnWaves;
+    static_assert(kDnRawChunks % (64 * kDnWaves) == 0 && SW % kKs == 0 && NS >= 3, "tiling");
+    __shared__ __align__(16) uint4 lds[kLdsChunks];
+
+    const int b = blockIdx.x;
+    const int sig = b % S;
+    const int t0 = (b / S) * kDnTok;
+    const int kbase = sig * SW;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const uint32_t lds0 = lds_addr(lds);
+
+    // W_down panel: wave instruction q (0..19) fills panel rows 16 q .. 16 q + 15
+    // (lane l: row 16 q + l / 4, chunk (l & 3) ^ ((row >> 2) & 3)); wave w
+    // issues q = w, w + 8 and (w < 4) w + 16.
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint16_t* wd_lane = W_down + (size_t)(lane >> 2) * kD + kbase + 8 * dchunk;
+    // raw R / pending: wave instruction q (0..15) fills rows 8 q .. 8 q + 7 (lane
+    // l: row 8 q + l / 8, chunk (l & 7) ^ swz8(row)); wave w issues q = w, w + 8.
+    // Rows past T re-read row T - 1 (their results are never stored).
+    const float* rraw[2];
+    const float* praw[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int q = wave + 8 * k;
+        const int row = 8 * q + (lane >> 3);
+        const int tr = t0 + row < T ? t0 + row : T - 1;
+        const int ch = (lane & 7) ^ swz8(row);
+        rraw[k] = R + (size_t)tr * kD + kbase + 4 * ch;
+        praw[k] = HAS_P ? P + (size_t)tr * kD + kbase + 4 * ch : nullptr;
+    }
+    auto issue_w = [&](int ks, int slot) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int q = wave + 8 * k;
+            if (k < 2 || wave < 4)
+                dma16(wd_lane + (size_t)(16 * q) * kD + kKs * ks, lds + kWOff + slot * kDnWChunks + 64 * q);
+        }
+    };
+    auto issue_raw = [&](int ks, int slot) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = wave + 8 * k;
+            dma16(rraw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + 64 * q);
+            if (HAS_P)
+                dma16(praw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + kDnRawChunks + 64 * q);
+        }
+    };
+
+    f32x4_t acc[20];
+#pragma unroll
+    for (int jb = 0; jb < 20; ++jb)
+        acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ssacc = 0.f;
+
+    // this lane's B operand: token 16 wave + n, columns 8 g .. 8 g + 7 of the step
+    const int trow = 16 * wave + n;
+    const bool tok_ok = t0 + trow < T;
+    const uint32_t raw_a = 16 * (trow * 8 + ((2 * g) ^ swz8(trow)));
+    const uint32_t raw_b = 16 * (trow * 8 + ((2 * g + 1) ^ swz8(trow)));
+    // W_down operand of row block jb: panel slot of row 16 jb + n, chunk g,
+    // i.e. this lane's slot in block 0 plus 1 KB per block
+    const uint32_t aoff = 16 * panel_slot(n, g);
+
+    auto compute = [&](int ks, int wslot, int rslot) {
+        const uint32_t rb = lds0 + 16 * (kRawOff + rslot * kRawSet);
+        u32x4 raw[6];
+        raw[0] = ds_read16(rb + raw_a);
+        raw[1] = ds_read16(rb + raw_b);
+        if (HAS_P) {
+            raw[2] = ds_read16(rb + 16 * kDnRawChunks + raw_a);
+            raw[3] = ds_read16(rb + 16 * kDnRawChunks + raw_b);
+        }
+        const uint32_t nb = lds0 + 16 * (kNormOff + 2 * (4 * ks + g));  // w_norm[32 ks + 8 g ..]
+        raw[4] = ds_read16(nb);
+        raw[5] = ds_read16(nb + 16);
+        const uint32_t wb = lds0 + 16 * (kWOff + wslot * kDnWChunks) + aoff;
+        u32x4 wa[5];
+        wa[0] = ds_read16_off<0>(wb);
+        wa[1] = ds_read16_off<1024>(wb);
+        wa[2] = ds_read16_off<2048>(wb);
+        wa[3] = ds_read16_off<3072>(wb);
+        wa[4] = ds_read16_off<4096>(wb);
+        lds_wait(raw);
+        // y = R' * w_norm, its square sum, and the exact 3-way split
+        uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = __uint_as_float(raw[e >> 2][e & 3]);
+            if (HAS_P)
+                x += __uint_as_float(raw[2 + (e >> 2)][e & 3]);
+            x = tok_ok ? x : 0.f;
+            ssacc += x * x;
+            split3(x * __uint_as_float(raw[4 + (e >> 2)][e & 3]), hi[e], mi[e], lo[e]);
+        }
+        u32x4 y[3];
+        y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
+        y[2] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+        // 4 groups of 5 row blocks: the next group's W_down operands are read
+        // while this group's 15 MFMAs run
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            u32x4 wn[5];
+            if (grp < 3) {
+                const uint32_t wg = wb + 5120 * (grp + 1);
+                wn[0] = ds_read16_off<0>(wg);
+                wn[1] = ds_read16_off<1024>(wg);
+                wn[2] = ds_read16_off<2048>(wg);
+                wn[3] = ds_read16_off<3072>(wg);
+                wn[4] = ds_read16_off<4096>(wg);
+                asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+#pragma unroll
+            for (int jb = 0; jb < 5; ++jb)
+                asm volatile("" : "+v"(wa[jb]));
+#pragma unroll
+            for (int p = 2; p >= 0; --p)
+#pragma unroll
+                for (int jb = 0; jb < 5; ++jb)
+                    acc[5 * grp + jb] = mfma16(wa[jb], y[p], acc[5 * grp + jb]);
+            if (grp < 3) {
+#pragma unroll
+                for (int jb = 0; jb < 5; ++jb)
+                    wa[jb] = wn[jb];
+            }
+        }
+    };
+
+    // Step ks: W_down of step ks + 1 is issued, then the raw activations of
+    // step ks + 2, so the wait at the end of the step leaves exactly those in
+    // flight; the matrix cores run step ks.
+    issue_w(0, 0);
+    if (64 * wave + lane < SW / 4)  // the split's w_norm, SW / 4 chunks
+        dma16(w_norm + kbase + 4 * (64 * wave + lane), lds + kNormOff + 64 * wave);
+    issue_raw(0, 0);
+    order();
+    issue_raw(1, 1);
+    ring_barrier<kRawLoads>();
+    int rs0 = 0;  // raw slot of step ks
+#pragma unroll 1
+    for (int ks = 0; ks < NS - 2; ++ks) {
+        issue_w(ks + 1, (ks + 1) & 1);
+        order();
+        issue_raw(ks + 2, rs0 == 0 ? 2 : rs0 - 1);  // (ks + 2) % 3
+        compute(ks, ks & 1, rs0);
+        ring_barrier<kRawLoads>();
+        rs0 = rs0 == 2 ? 0 : rs0 + 1;
+    }
+    issue_w(NS - 1, (NS - 1) & 1);
+    compute(NS - 2, (NS - 2) & 1, rs0);
+    ring_barrier<0>();
+    compute(NS - 1, (NS - 1) & 1, rs0 == 2 ? 0 : rs0 + 1);
+
+    // partials: lane holds token t0 + 16 wave + n, rows 16 jb + 4 g .. +3
+    const int t = t0 + trow;
+    if (tok_ok) {
+        float* dst = part + ((size_t)sig * T + t) * kRank + 4 * g;
+#pragma unroll
+        for (int jb = 0; jb < 20; ++jb)
+            *reinterpret_cast<f32x4_t*>(dst + 16 * jb) = acc[jb];
+    }
+    // sum of squares of the token: lanes n, n + 16, n + 32, n + 48
+    const float s1 = ssacc + __shfl_xor(ssacc, 16);
+    const float s2 = s1 + __shfl_xor(s1, 32);
+    if (g == 0 && tok_ok)
+        ssq[(size_t)sig * T + t] = s2;
+}
+
+// ---------------------------------------------------------------------------
+// P2: lo = sum_s rs_s * stream partial, as three bf16 planes in the tiled
+// layout: for token tile u and K step ks, the three plane panels of 64 rows
+// (tokens) x 4 chunks, 12 KB contiguous at chunk ((u * 10 + ks) * 3) * 256.
+// Tokens of the last tile past T get zeros.
 // ---------------------------------------------------------------------------
 template <int S>
-__global__ __launch_bounds__(256) void prefill_down(int T, const float* __restrict__ R,
-                                                    const float* __restrict__ P,
-                                                    const float* __restrict__ w_norm,
-                                                    const uint16_t* __restrict__ W_down,
-                                                    float* __restrict__ part, float* __restrict__ ssq)
+__global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* __restrict__ part,
+                                                  const float* __restrict__ ssq, uint4* __restrict__ planes)
 {
-    constexpr int KW = kWidth / S;  // columns of one split
-    constexpr int KSTEPS = KW / 32;
-    __shared__ __align__(16) uint16_t ypl[2][3][kP1Tok][kP1Row];
-
-    const int bid = blockIdx.x;
-    const int x = bid & 7;  // XCD: every workgroup of one split on one or two XCDs
-    int sig, tile;
-    if (S == 2) {
-        sig = x;
-        tile = bid >> 3;
-    } else {
-        sig = x & 3;
-        tile = (bid >> 3) * 2 + (x >> 2);
-    }
-    const int t0 = tile * kP1Tok;
-    if (t0 >= T)
+    constexpr int Q = S / 4;  // splits per stream
+    const int idx = blockIdx.x * 256 + threadIdx.x;  // (token, chunk of 8 rank indices)
+    const int t = idx / (kRank / 8);
+    const int c8 = idx - t * (kRank / 8);
+    if (t >= Tpad)
         return;
-    const int kbase = (sig / S) * kWidth + (sig % S) * KW;  // first flattened column
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, g = lane >> 4;
-    // staging role: token row r, 8 columns c8
-    const int r = tid >> 2, c8 = (tid & 3) * 8;
-    const int tr = t0 + r;
-    const bool row_ok = tr < T;
-
-    float ssacc = 0.f;
-    float4 sr0, sr1, sp0, sp1, sw0, sw1;
-    auto load_stage = [&](int ks) {
-        const int k = kbase + ks * 32 + c8;
-        sw0 = *reinterpret_cast<const float4*>(w_norm + k);
-        sw1 = *reinterpret_cast<const float4*>(w_norm + k + 4);
-        if (row_ok) {
-            sr0 = *reinterpret_cast<const float4*>(R + (size_t)tr * kD + k);
-            sr1 = *reinterpret_cast<const float4*>(R + (size_t)tr * kD + k + 4);
-            if (P) {
-                sp0 = *reinterpret_cast<const float4*>(P + (size_t)tr * kD + k);
-                sp1 = *reinterpret_cast<const float4*>(P + (size_t)tr * kD + k + 4);
-            }
-        }
-    };
-    auto store_stage = [&](int buf) {
-        uint32_t hi[8], mi[8], lo[8];
-        if (row_ok) {
-            float v[8] = {sr0.x, sr0.y, sr0.z, sr0.w, sr1.x, sr1.y, sr1.z, sr1.w};
-            if (P) {
-                v[0] += sp0.x; v[1] += sp0.y; v[2] += sp0.z; v[3] += sp0.w;
-                v[4] += sp1.x; v[5] += sp1.y; v[6] += sp1.z; v[7] += sp1.w;
-            }
-            const float w[8] = {sw0.x, sw0.y, sw0.z, sw0.w, sw1.x, sw1.y, sw1.z, sw1.w};
+    float lo[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                ssacc += v[e] * v[e];
-                split3(v[e] * w[e], hi[e], mi[e], lo[e]);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                hi[e] = mi[e] = lo[e] = 0;
-        }
-        *reinterpret_cast<uint4*>(&ypl[buf][0][r][c8]) =
-            make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-        *reinterpret_cast<uint4*>(&ypl[buf][1][r][c8]) =
-            make_uint4(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16));
-        *reinterpret_cast<uint4*>(&ypl[buf][2][r][c8]) =
-            make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-    };
-    // this wave's rows: 16 * (5 wave + nb) + n
-    const uint16_t* wrow[5];
-#pragma unroll
-    for (int nb = 0; nb < 5; ++nb)
-        wrow[nb] = W_down + (size_t)(16 * (5 * wave + nb) + n) * kD + kbase + 8 * g;
-    uint4 wb[5], wn[5];
-    auto load_b = [&](int ks, uint4 (&dst)[5]) {
-#pragma unroll
-        for (int nb = 0; nb < 5; ++nb)
-            dst[nb] = *reinterpret_cast<const uint4*>(wrow[nb] + ks * 32);
-    };
-
-    f32x4_t acc[4][5];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 5; ++nb)
-            acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    load_stage(0);
-    load_b(0, wb);
-    store_stage(0);
-    __syncthreads();
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int buf = ks & 1;
-        const bool more = ks + 1 < KSTEPS;
-        if (more) {
-            load_stage(ks + 1);
-            load_b(ks + 1, wn);
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int m = 16 * mb + (lane & 15);
-            const uint4 ah = *reinterpret_cast<const uint4*>(&ypl[buf][0][m][8 * g]);
-            const uint4 am = *reinterpret_cast<const uint4*>(&ypl[buf][1][m][8 * g]);
-            const uint4 al = *reinterpret_cast<const uint4*>(&ypl[buf][2][m][8 * g]);
-#pragma unroll
-            for (int nb = 0; nb < 5; ++nb) {
-                acc[mb][nb] = mfma16(al, wb[nb], acc[mb][nb]);
-                acc[mb][nb] = mfma16(am, wb[nb], acc[mb][nb]);
-                acc[mb][nb] = mfma16(ah, wb[nb], acc[mb][nb]);
-            }
-        }
-        if (more) {
-            store_stage(buf ^ 1);
-#pragma unroll
-            for (int nb = 0; nb < 5; ++nb)
-                wb[nb] = wn[nb];
-        }
-        __syncthreads();
-    }
-
-    // partials: D rows = tokens 16 mb + 4 g + i, columns = rows of W_down
-    float* pdst = part + (size_t)sig * T * kRank;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * mb + 4 * g + i;
-            if (t < T)
-#pragma unroll
-                for (int nb = 0; nb < 5; ++nb)
-                    pdst[(size_t)t * kRank + 16 * (5 * wave + nb) + n] = acc[mb][nb][i];
-        }
-    // sums of squares: the 4 staging threads of a token row are one quad
-    const float ss = sum4(ssacc);
-    if ((tid & 3) == 0 && row_ok)
-        ssq[(size_t)sig * T + tr] = ss;
-}
-
-// ---------------------------------------------------------------------------
-// P2: lo = sum_s rs_s * stream partial, as three bf16 planes.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prefill_lo(int T, int S, const float* __restrict__ part,
-                                                  const float* __restrict__ ssq,
-                                                  uint16_t* __restrict__ planes)
-{
-    const int idx = blockIdx.x * 256 + threadIdx.x;  // (token, pair of rank indices)
-    const int t = idx / (kRank / 2);
-    if (t >= T)
-        return;
-    const int j = 2 * (idx % (kRank / 2));
-    float v0[4], v1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        float ss = 0.f, p0 = 0.f, p1 = 0.f;
-        for (int q = 0; q < S; ++q) {
-            const int sig = s * S + q;
-            ss += ssq[(size_t)sig * T + t];
-            const float2 pv = *reinterpret_cast<const float2*>(part + ((size_t)sig * T + t) * kRank + j);
-            p0 += pv.x;
-            p1 += pv.y;
-        }
-        const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
-        v0[s] = p0 * rs;
-        v1[s] = p1 * rs;
-    }
-    const float lo0 = (v0[0] + v0[1]) + (v0[2] + v0[3]);
-    const float lo1 = (v1[0] + v1[1]) + (v1[2] + v1[3]);
-    uint32_t h0, m0, l0, h1, m1, l1;
-    split3(lo0, h0, m0, l0);
-    split3(lo1, h1, m1, l1);
-    const size_t o = (size_t)t * kRank + j;
-    const size_t plane = (size_t)T * kRank;
-    *reinterpret_cast<uint32_t*>(planes + o) = h0 | (h1 << 16);
-    *reinterpret_cast<uint32_t*>(planes + plane + o) = m0 | (m1 << 16);
-    *reinterpret_cast<uint32_t*>(planes + 2 * plane + o) = l0 | (l1 << 16);
-}
-
-// ---------------------------------------------------------------------------
-// P3: up projection with the stream mix as its epilogue.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prefill_upmix(int T, const uint16_t* __restrict__ planes,
-                                                     const uint16_t* __restrict__ W_up,
-                                                     const float* __restrict__ R,
-                                                     const float* __restrict__ P,
-                                                     float* __restrict__ out_mixed,
-                                                     uint16_t* __restrict__ out_bf16,
-                                                     uint16_t* __restrict__ out_fp16)
-{
-    __shared__ __align__(16) float upt[kP3Tok][4][kP3Cols + 4];  // up, transposed for the mix
-
-    const int bid = blockIdx.x;
-    const int x = bid & 7, jj = bid >> 3;  // a token tile's workgroups share an XCD
-    const int tile = x + 8 * (jj / kP3ColTiles);
-    const int t0 = tile * kP3Tok;
-    if (t0 >= T)
-        return;
-    const int c0 = (jj % kP3ColTiles) * kP3Cols;
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, g = lane >> 4;
-    const size_t plane = (size_t)T * kRank;
-
-    // A rows: tokens t0 + 32 wave + 16 mb + (lane & 15)
-    const uint16_t* arow[2];
-    bool aok[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int t = t0 + 32 * wave + 16 * mb + (lane & 15);
-        aok[mb] = t < T;
-        arow[mb] = planes + (size_t)(aok[mb] ? t : 0) * kRank + 8 * g;
-    }
-    // B rows: MFMA column slot n of block nb = column c0 + 4 nb + n / 4, stream n % 4
-    const uint16_t* brow[8];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-        brow[nb] = W_up + (size_t)((n & 3) * kWidth + c0 + 4 * nb + (n >> 2)) * kRank + 8 * g;
-
-    uint4 a[2][3], an[2][3], b[8], bn[8];
-    auto load_ab = [&](int q, uint4 (&ad)[2][3], uint4 (&bd)[8]) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-                ad[mb][p] = aok[mb] ? *reinterpret_cast<const uint4*>(arow[mb] + p * plane + 32 * q)
-                                    : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-            bd[nb] = *reinterpret_cast<const uint4*>(brow[nb] + 32 * q);
-    };
-
-    f32x4_t acc[2][8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-            acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    load_ab(0, a, b);
-#pragma unroll 1
-    for (int q = 0; q < kRank / 32; ++q) {
-        const bool more = q + 1 < kRank / 32;
-        if (more)
-            load_ab(q + 1, an, bn);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                acc[mb][nb] = mfma16(a[mb][2], b[nb], acc[mb][nb]);
-                acc[mb][nb] = mfma16(a[mb][1], b[nb], acc[mb][nb]);
-                acc[mb][nb] = mfma16(a[mb][0], b[nb], acc[mb][nb]);
-            }
-        if (more) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    a[mb][p] = an[mb][p];
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-                b[nb] = bn[nb];
-        }
-    }
-
-    // gated = up (identity epilogue): transpose through LDS as [token][stream][column]
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                upt[32 * wave + 16 * mb + 4 * g + i][n & 3][4 * nb + (n >> 2)] = acc[mb][nb][i];
-    __syncthreads();
-
-    // mix: each item = one token and 4 consecutive columns
-#pragma unroll
-    for (int it = 0; it < kP3Tok * (kP3Cols / 4) / 256; ++it) {
-        const int item = tid + 256 * it;
-        const int tl = item / (kP3Cols / 4);
-        const int cg = 4 * (item % (kP3Cols / 4));
-        const int t = t0 + tl;
-        if (t >= T)
-            continue;
-        const int c = c0 + cg;
-        float4 m[4];
+    for (int e = 0; e < 8; ++e)
+        lo[e] = 0.f;
+    if (t < T) {
+        float v[4][8];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            float4 rv = *reinterpret_cast<const float4*>(R + (size_t)t * kD + s * kWidth + c);
-            if (P) {
-                const float4 pv = *reinterpret_cast<const float4*>(P + (size_t)t * kD + s * kWidth + c);
-                rv.x += pv.x;
-                rv.y += pv.y;
-                rv.z += pv.z;
-                rv.w += pv.w;
+            float ss = 0.f, sum[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sum[e] = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int sg = Q * s + q;
+                ss += ssq[(size_t)sg * T + t];
+                const float* pp = part + ((size_t)sg * T + t) * kRank + 8 * c8;
+                const float4 a0 = *reinterpret_cast<const float4*>(pp), a1 = *reinterpret_cast<const float4*>(pp + 4);
+                const float pv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sum[e] += pv[e];
             }
-            const float4 u = *reinterpret_cast<const float4*>(&upt[tl][s][cg]);
-            m[s] = make_float4(u.x * rv.x, u.y * rv.y, u.z * rv.z, u.w * rv.w);
+            const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[s][e] = sum[e] * rs;
         }
-        const float4 mixed = make_float4((m[0].x + m[1].x) + (m[2].x + m[3].x),
-                                         (m[0].y + m[1].y) + (m[2].y + m[3].y),
-                                         (m[0].z + m[1].z) + (m[2].z + m[3].z),
-                                         (m[0].w + m[1].w) + (m[2].w + m[3].w));
-        const size_t o = (size_t)t * kWidth + c;
-        *reinterpret_cast<float4*>(out_mixed + o) = mixed;
-        const uint16_t b0 = __builtin_bit_cast(uint16_t, (__bf16)mixed.x);
-        const uint16_t b1 = __builtin_bit_cast(uint16_t, (__bf16)mixed.y);
-        const uint16_t b2 = __builtin_bit_cast(uint16_t, (__bf16)mixed.z);
-        const uint16_t b3 = __builtin_bit_cast(uint16_t, (__bf16)mixed.w);
-        *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
-        const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)mixed.x);
-        const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)mixed.y);
-        const uint16_t h2 = __builtin_bit_cast(uint16_t, (_Float16)mixed.z);
-        const uint16_t h3 = __builtin_bit_cast(uint16_t, (_Float16)mixed.w);
-        *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            lo[e] = (v[0][e] + v[1][e]) + (v[2][e] + v[3][e]);
     }
+    uint32_t hi[8], mi[8], l3[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        split3(lo[e], hi[e], mi[e], l3[e]);
+    const int tile = t / kTok, tl = t - tile * kTok;
+    const int ks = c8 >> 2, c = c8 & 3;
+    uint4* dst = planes + (size_t)(tile * kUpSteps + ks) * kLoBlock + panel_slot(tl, c);
+    dst[0] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+    dst[kPlaneChunks] = make_uint4(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16));
+    dst[2 * kPlaneChunks] = make_uint4(l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16));
+}
+
+// ---------------------------------------------------------------------------
+// P3: up projection with the stream mix as its epilogue.  Workgroup b: XCD
+// x = b % 8, q = b / 8: token tile q / 5, column group x + 8 (q % 5) (64
+// columns).  Wave w computes columns c0 + 16 w .. +15 of all 4 streams for
+// all 64 tokens: MFMA A = W_up rows (one block per stream), B = lo planes (4
+// token blocks x 3 pieces); D then holds, in lane (n, g), token 16 tb + n and
+// columns 4 g .. 4 g + 3 of every stream, so the mix is per lane.
+// LDS stage (28 KB): W_up panel (256 rows: row 64 s + j = W_up row
+// s * 2560 + c0 + j, 16 KB), then the 3 lo panels (12 KB).
+// ---------------------------------------------------------------------------
+constexpr int kUpWChunks = 4 * kUpCols * 4;      // 1024
+constexpr int kUpStage = kUpWChunks + kLoBlock;  // 1792 chunks
+
+template <bool HAS_P>
+__global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ planes,
+                                                        const uint16_t* __restrict__ W_up,
+                                                        const float* __restrict__ R,
+                                                        const float* __restrict__ P,
+                                                        float* __restrict__ out_mixed,
+                                                        uint16_t* __restrict__ out_bf16,
+                                                        uint16_t* __restrict__ out_fp16)
+{
+    __shared__ __align__(16) uint4 lds[2 * kUpStage];
+
+    const int b = blockIdx.x;
+    const int x = b & 7, q = b >> 3;
+    const int tile = q / kGroupsPerXcd;
+    const int cg = x + 8 * (q - tile * kGroupsPerXcd);
+    const int t0 = tile * kTok, c0 = cg * kUpCols;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+
+    // stage loads: wave instruction i (0..27): i < 16 fills W_up panel rows
+    // 16 i .. 16 i + 15 (lane l: row 16 i + l / 4, chunk (l & 3) ^ ((row >> 2) & 3));
+    // i >= 16 copies 1 KB of the lo block.  Wave w issues i = w + 4 k.
+    const int wchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint16_t* wu_lane[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int prow = 16 * (wave + 4 * k) + (lane >> 2);  // panel row = 64 s + j
+        wu_lane[k] = W_up + (size_t)((prow >> 6) * kWidth + c0 + (prow & 63)) * kRank + 8 * wchunk;
+    }
+    const uint4* lo_lane = planes + (size_t)tile * kUpSteps * kLoBlock + lane;
+    auto issue = [&](int ks, int stage) {
+        uint4* sb = lds + stage * kUpStage;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            dma16(wu_lane[k] + kKs * ks, sb + 64 * (wave + 4 * k));
+#pragma unroll
+        for (int k = 4; k < 7; ++k) {
+            const int i = wave + 4 * k - 16;  // 1 KB piece of the lo block, 0..11
+            dma16(lo_lane + (size_t)ks * kLoBlock + 64 * i, sb + kUpWChunks + 64 * i);
+        }
+    };
+
+    f32x4_t acc[4][4];  // [token block][stream]
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc[tb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint32_t lds0 = lds_addr(lds);
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        aoff[s] = 16 * panel_slot(64 * s + 16 * wave + n, g);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+        boff[tb] = 16 * (kUpWChunks + panel_slot(16 * tb + n, g));
+    auto compute = [&](int stage) {
+        const uint32_t sb = lds0 + 16 * stage * kUpStage;
+        u32x4 op[16];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            op[s] = ds_read16(sb + aoff[s]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                op[4 + 3 * tb + p] = ds_read16(sb + boff[tb] + 16 * kPlaneChunks * p);
+        lds_wait(op);
+#pragma unroll
+        for (int p = 2; p >= 0; --p)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc[tb][s] = mfma16(op[s], op[4 + 3 * tb + p], acc[tb][s]);
+    };
+
+    issue(0, 0);
+    ring_barrier<0>();
+#pragma unroll 1
+    for (int ks = 0; ks < kUpSteps - 1; ++ks) {
+        issue(ks + 1, (ks + 1) & 1);
+        compute(ks & 1);
+        ring_barrier<0>();
+    }
+    compute((kUpSteps - 1) & 1);
+
+    // gated = up (identity epilogue); mixed = sum_s gated_s * R'_s, then images.
+    // Every R (and pending) load is issued before the first use (tokens past
+    // T re-read token T - 1 and store nothing).
+    const int c = c0 + 16 * wave + 4 * g;
+    float4 rv[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int t = t0 + 16 * tb + n < T ? t0 + 16 * tb + n : T - 1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            rv[tb][s] = *reinterpret_cast<const float4*>(R + (size_t)t * kD + s * kWidth + c);
+    }
+    if (HAS_P) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t = t0 + 16 * tb + n < T ? t0 + 16 * tb + n : T - 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float4 pv = *reinterpret_cast<const float4*>(P + (size_t)t * kD + s * kWidth + c);
+                rv[tb][s].x += pv.x;
+                rv[tb][s].y += pv.y;
+                rv[tb][s].z += pv.z;
+                rv[tb][s].w += pv.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int t = t0 + 16 * tb + n;
+        const float r[4][4] = {{rv[tb][0].x, rv[tb][0].y, rv[tb][0].z, rv[tb][0].w},
+                               {rv[tb][1].x, rv[tb][1].y, rv[tb][1].z, rv[tb][1].w},
+                               {rv[tb][2].x, rv[tb][2].y, rv[tb][2].z, rv[tb][2].w},
+                               {rv[tb][3].x, rv[tb][3].y, rv[tb][3].z, rv[tb][3].w}};
+        float m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m[i] = (acc[tb][0][i] * r[0][i] + acc[tb][1][i] * r[1][i]) +
+                   (acc[tb][2][i] * r[2][i] + acc[tb][3][i] * r[3][i]);
+        if (t < T) {
+            const size_t o = (size_t)t * kWidth + c;
+            *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
+            uint32_t bh[4], hh[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
+                hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
+            }
+            *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
+            *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+    }
+}
+
+int tiles_of(int tokens)
+{
+    return (tokens + kTok - 1) / kTok;
+}
+
+// P1's split count: stream halves when that already gives a workgroup per
+// CU, else stream quarters.
+int splits_for(int tokens)
+{
+    return (tokens + kDnTok - 1) / kDnTok * 8 >= 256 ? 8 : 16;
+}
+
+// (split, token) slots of the partial array, enough for any chunk of up to
+// `chunk` tokens
+size_t part_slots(int chunk)
+{
+    size_t most = 0;
+    for (int tc = chunk; tc > 0; tc -= kDnTok) {  // splits_for changes only at tile boundaries
+        const size_t n = (size_t)splits_for(tc) * tc;
+        most = most > n ? most : n;
+    }
+    return most;
 }
 
 }  // namespace
 
 size_t prefill_scratch_bytes(int chunk)
 {
-    // S = 2 at most: 8 splits of partials and sums of squares, 3 lo planes
-    return sizeof(float) * ((size_t)8 * chunk * kRank + (size_t)8 * chunk) +
-           sizeof(uint16_t) * (size_t)3 * chunk * kRank + 256;
+    const size_t tpad = (size_t)tiles_of(chunk) * kTok;
+    return sizeof(float) * part_slots(chunk) * (kRank + 1) + sizeof(uint16_t) * 3 * tpad * kRank + 512;
 }
 
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
@@ -413,38 +601,48 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
                           uint16_t* out_bf16, uint16_t* out_fp16, void* scratch, int chunk,
                           hipStream_t stream)
 {
-    float* part = static_cast<float*>(scratch);
-    float* ssq = part + (size_t)8 * chunk * kRank;
-    uint16_t* planes = reinterpret_cast<uint16_t*>(ssq + (size_t)8 * chunk);
+    const size_t slots = part_slots(chunk);
+    float* part = static_cast<float*>(scratch);  // [S][Tc][320]
+    float* ssq = part + slots * kRank;             // [S][Tc]
+    uint4* planes = reinterpret_cast<uint4*>(      // tiled lo planes
+        (reinterpret_cast<uintptr_t>(ssq + slots) + 255) & ~uintptr_t(255));
     for (int64_t c0 = 0; c0 < T; c0 += chunk) {
         const int Tc = (int)(T - c0 < chunk ? T - c0 : chunk);
         const size_t in_off = (size_t)c0 * kD, out_off = (size_t)c0 * kWidth;
         const float* Rc = R + in_off;
         const float* Pc = P ? P + in_off : nullptr;
-        const int tiles1 = (Tc + kP1Tok - 1) / kP1Tok;
-        // one split per stream when that already fills the chip, else two
-        const int S = tiles1 * 4 >= 256 ? 1 : 2;
-        if (S == 1) {
-            const int grid = 8 * ((tiles1 + 1) / 2);
-            hipLaunchKernelGGL(prefill_down<1>, dim3(grid), dim3(256), 0, stream, Tc, Rc, Pc, w_norm,
-                               W_down, part, ssq);
+        const int S = splits_for(Tc);
+        const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
+        if (S == 8) {
+            if (Pc)
+                hipLaunchKernelGGL((prefill_down<8, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+            else
+                hipLaunchKernelGGL((prefill_down<8, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
         } else {
-            hipLaunchKernelGGL(prefill_down<2>, dim3(8 * tiles1), dim3(256), 0, stream, Tc, Rc, Pc,
-                               w_norm, W_down, part, ssq);
+            if (Pc)
+                hipLaunchKernelGGL((prefill_down<16, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+            else
+                hipLaunchKernelGGL((prefill_down<16, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        const int items = Tc * (kRank / 2);
-        hipLaunchKernelGGL(prefill_lo, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, S, part, ssq,
-                           planes);
+        const int tiles = tiles_of(Tc);
+        const int items = tiles * kTok * (kRank / 8);
+        if (S == 8)
+            hipLaunchKernelGGL(prefill_lo<8>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq, planes);
+        else
+            hipLaunchKernelGGL(prefill_lo<16>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq, planes);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        const int tiles3 = (Tc + kP3Tok - 1) / kP3Tok;
-        const int grid3 = 8 * kP3ColTiles * ((tiles3 + 7) / 8);
-        hipLaunchKernelGGL(prefill_upmix, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
-                           out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off);
+        const int grid3 = 8 * kGroupsPerXcd * tiles;
+        if (Pc)
+            hipLaunchKernelGGL(prefill_upmix<true>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
+                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off);
+        else
+            hipLaunchKernelGGL(prefill_upmix<false>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
+                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
