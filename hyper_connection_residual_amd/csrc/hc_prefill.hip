@@ -28,10 +28,12 @@
 //   ds_read_b128 and every wait is explicit: the compiler, seeing an LDS read
 //   that may alias a load still landing in LDS, would wait for ALL loads in
 //   flight (vmcnt(0)) and serialise the ring.
-// * Inside LDS a K step of a tile is a "panel": one row per matrix row, four
-//   16-byte chunks per row, chunk c of row r stored at slot 4 r + (c ^ ((r >>
-//   2) & 3)).  The 16 lanes that read one chunk column of 16 consecutive rows
-//   then hit 16 distinct 16-byte bank groups.
+// * Inside LDS a K step of a weight tile is a "panel": one row per matrix
+//   row, four 16-byte chunks per row, chunk c of row r stored at slot
+//   4 r + (c ^ ((r >> 1) & 3)).  LDS serves a 16-byte read to 8 lanes per
+//   cycle; the 8 lanes that read one chunk column of 8 consecutive rows then
+//   hit distinct bank groups (measured: the swizzle by r >> 2 instead left
+//   ~45 % of LDS cycles in bank conflicts).
 // * Both kernels use 4 waves and 56-64 KB of LDS, so two workgroups share a
 //   CU: one's epilogue (memory bound) overlaps the other's matrix work.
 // * XCD-aware grids (workgroup b runs on XCD b % 8): P1's XCD x owns split x,
@@ -120,10 +122,21 @@ __device__ __forceinline__ void dma16(const void* g, uint4* lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
 }
 
-// Slot (in 16-byte chunks) of chunk c (0..3) of row r in a panel.
+// Slot (in 16-byte chunks) of chunk c (0..3) of row r in a panel.  LDS
+// serves a 16-byte read to 8 lanes per cycle (128 bytes, 32 banks); the 8
+// lanes reading chunk c of 8 consecutive rows (two rows per 128 bytes) then
+// hit 8 distinct 16-byte bank groups.
 __host__ __device__ constexpr int panel_slot(int r, int c)
 {
-    return 4 * r + (c ^ ((r >> 2) & 3));
+    return 4 * r + (c ^ ((r >> 1) & 3));
+}
+
+// Slot (0..7) of chunk 0 of row r in a 128-byte line of 8 chunks: chunk c of
+// row r is stored at slot c ^ swz8(r), so 16 lanes reading one chunk of 16
+// consecutive rows hit distinct 16-byte bank groups.
+__host__ __device__ constexpr int swz8(int row)
+{
+    return (row & 7) ^ ((row >> 3) & 1);
 }
 
 constexpr int kTok = 64;                       // token tile of both matrix kernels
@@ -132,8 +145,7 @@ constexpr int kUpSteps = kRank / kKs;          // 10
 constexpr int kUpCols = 64;                    // P3 output columns per tile
 constexpr int kUpGroups = kWidth / kUpCols;    // 40 column groups
 constexpr int kGroupsPerXcd = kUpGroups / 8;   // 5
-constexpr int kPlaneChunks = kTok * 4;         // one plane panel of a token tile: 256 chunks (4 KB)
-constexpr int kLoBlock = 3 * kPlaneChunks;     // the three planes of one (tile, K step): 12 KB
+constexpr int kLoTile = kTok * 8;              // fp32 lo of one (token tile, K step): 512 chunks (8 KB)
 
 // ---------------------------------------------------------------------------
 // P1: down projection partials and sums of squares.  Workgroup b: split
@@ -144,8 +156,10 @@ constexpr int kLoBlock = 3 * kPlaneChunks;     // the three planes of one (tile,
 // w_norm, split in registers into its three bf16 pieces (each wave converts
 // only its own tokens, so no y panel is shared through LDS).
 // Everything reaches LDS by direct loads: the W_down panel of a step one step
-// ahead (2 slots), raw R and pending two steps ahead (3 slots), and the
-// split's w_norm once.  No loaded value lives in registers across a step.
+// ahead (2 slots), raw R and pending three steps ahead (3 slots), and the
+// split's w_norm once.  No loaded value lives in registers across a step;
+// the converted y of the next step does (it is computed while the matrix
+// cores run the current one).
 // Raw rows are 32 floats (8 chunks of 16 bytes); chunk c of row r sits at slot
 // c ^ swz(r) of its 128-byte line, so 16 lanes reading one chunk of 16 rows
 // hit distinct bank groups.
@@ -154,11 +168,6 @@ constexpr int kDnTok = 128;
 constexpr int kDnWaves = 8;
 constexpr int kDnWChunks = kRank * 4;           // W_down panel: 1280 chunks (20 KB)
 constexpr int kDnRawChunks = kDnTok * 8;        // raw R (or pending) of a step: 1024 chunks (16 KB)
-
-__device__ __forceinline__ int swz8(int row)
-{
-    return (row & 7) ^ ((row >> 3) & 1);
-}
 
 template <int S, bool HAS_P>
 __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float* __restrict__ R,
@@ -191,9 +200,9 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
     const uint32_t lds0 = lds_addr(lds);
 
     // W_down panel: wave instruction q (0..19) fills panel rows 16 q .. 16 q + 15
-    // (lane l: row 16 q + l / 4, chunk (l & 3) ^ ((row >> 2) & 3)); wave w
+    // (lane l: row 16 q + l / 4, chunk (l & 3) ^ ((row >> 1) & 3)); wave w
     // issues q = w, w + 8 and (w < 4) w + 16.
-    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
     const uint16_t* wd_lane = W_down + (size_t)(lane >> 2) * kD + kbase + 8 * dchunk;
     // raw R / pending: wave instruction q (0..15) fills rows 8 q .. 8 q + 7 (lane
     // l: row 8 q + l / 8, chunk (l & 7) ^ swz8(row)); wave w issues q = w, w + 8.
@@ -242,7 +251,9 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
     // i.e. this lane's slot in block 0 plus 1 KB per block
     const uint32_t aoff = 16 * panel_slot(n, g);
 
-    auto compute = [&](int ks, int wslot, int rslot) {
+    // y = R' * w_norm of step ks for this lane, split into its three bf16
+    // pieces (and the square sum accumulated), from raw slot rslot
+    auto convert = [&](int ks, int rslot, u32x4 (&y)[3]) {
         const uint32_t rb = lds0 + 16 * (kRawOff + rslot * kRawSet);
         u32x4 raw[6];
         raw[0] = ds_read16(rb + raw_a);
@@ -254,15 +265,7 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
         const uint32_t nb = lds0 + 16 * (kNormOff + 2 * (4 * ks + g));  // w_norm[32 ks + 8 g ..]
         raw[4] = ds_read16(nb);
         raw[5] = ds_read16(nb + 16);
-        const uint32_t wb = lds0 + 16 * (kWOff + wslot * kDnWChunks) + aoff;
-        u32x4 wa[5];
-        wa[0] = ds_read16_off<0>(wb);
-        wa[1] = ds_read16_off<1024>(wb);
-        wa[2] = ds_read16_off<2048>(wb);
-        wa[3] = ds_read16_off<3072>(wb);
-        wa[4] = ds_read16_off<4096>(wb);
         lds_wait(raw);
-        // y = R' * w_norm, its square sum, and the exact 3-way split
         uint32_t hi[8], mi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -273,12 +276,20 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
             ssacc += x * x;
             split3(x * __uint_as_float(raw[4 + (e >> 2)][e & 3]), hi[e], mi[e], lo[e]);
         }
-        u32x4 y[3];
         y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
         y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
         y[2] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
-        // 4 groups of 5 row blocks: the next group's W_down operands are read
-        // while this group's 15 MFMAs run
+    };
+    // The 60 MFMAs of a step on y: 4 groups of 5 row blocks, the next group's
+    // W_down operands read while this group's 15 MFMAs run.
+    auto mma = [&](int wslot, const u32x4 (&y)[3]) {
+        const uint32_t wb = lds0 + 16 * (kWOff + wslot * kDnWChunks) + aoff;
+        u32x4 wa[5];
+        wa[0] = ds_read16_off<0>(wb);
+        wa[1] = ds_read16_off<1024>(wb);
+        wa[2] = ds_read16_off<2048>(wb);
+        wa[3] = ds_read16_off<3072>(wb);
+        wa[4] = ds_read16_off<4096>(wb);
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
             u32x4 wn[5];
@@ -310,29 +321,48 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
     };
 
     // Step ks: W_down of step ks + 1 is issued, then the raw activations of
-    // step ks + 2, so the wait at the end of the step leaves exactly those in
-    // flight; the matrix cores run step ks.
+    // step ks + 3 (the wait at the end of the step leaves exactly those in
+    // flight); the matrix cores run step ks on y, computed during step ks - 1,
+    // while step ks + 1's raw slot (landed by the previous wait) is turned
+    // into the next y.  Raw slot of step k: k % 3 (step k + 3 reuses step k's
+    // slot, converted during step k - 1).
     issue_w(0, 0);
     if (64 * wave + lane < SW / 4)  // the split's w_norm, SW / 4 chunks
         dma16(w_norm + kbase + 4 * (64 * wave + lane), lds + kNormOff + 64 * wave);
     issue_raw(0, 0);
-    order();
     issue_raw(1, 1);
+    order();
+    issue_raw(2, 2);
     ring_barrier<kRawLoads>();
-    int rs0 = 0;  // raw slot of step ks
+    u32x4 ycur[3], ynext[3];
+    convert(0, 0, ycur);
+    ring_barrier<kRawLoads>();  // every wave is done with raw slot 0 before step 0 refills it
+    int rs1 = 1;  // raw slot of step ks + 1
 #pragma unroll 1
-    for (int ks = 0; ks < NS - 2; ++ks) {
+    for (int ks = 0; ks < NS - 3; ++ks) {
         issue_w(ks + 1, (ks + 1) & 1);
         order();
-        issue_raw(ks + 2, rs0 == 0 ? 2 : rs0 - 1);  // (ks + 2) % 3
-        compute(ks, ks & 1, rs0);
+        issue_raw(ks + 3, rs1 == 0 ? 2 : rs1 - 1);  // (ks + 3) % 3 == ks % 3
+        convert(ks + 1, rs1, ynext);
+        mma(ks & 1, ycur);
         ring_barrier<kRawLoads>();
-        rs0 = rs0 == 2 ? 0 : rs0 + 1;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            ycur[p] = ynext[p];
+        rs1 = rs1 == 2 ? 0 : rs1 + 1;
     }
-    issue_w(NS - 1, (NS - 1) & 1);
-    compute(NS - 2, (NS - 2) & 1, rs0);
-    ring_barrier<0>();
-    compute(NS - 1, (NS - 1) & 1, rs0 == 2 ? 0 : rs0 + 1);
+#pragma unroll
+    for (int ks = NS - 3; ks < NS - 1; ++ks) {  // nothing more to load after step NS - 1's raw slot
+        issue_w(ks + 1, (ks + 1) & 1);
+        convert(ks + 1, rs1, ynext);
+        mma(ks & 1, ycur);
+        ring_barrier<0>();
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            ycur[p] = ynext[p];
+        rs1 = rs1 == 2 ? 0 : rs1 + 1;
+    }
+    mma((NS - 1) & 1, ycur);
 
     // partials: lane holds token t0 + 16 wave + n, rows 16 jb + 4 g .. +3
     const int t = t0 + trow;
@@ -350,80 +380,71 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
 }
 
 // ---------------------------------------------------------------------------
-// P2: lo = sum_s rs_s * stream partial, as three bf16 planes in the tiled
-// layout: for token tile u and K step ks, the three plane panels of 64 rows
-// (tokens) x 4 chunks, 12 KB contiguous at chunk ((u * 10 + ks) * 3) * 256.
-// Tokens of the last tile past T get zeros.
+// P2: lo = sum_s rs_s * stream partial (fp32), in the tiled layout P3 copies
+// into LDS verbatim: for token tile u (64 tokens) and K step ks, 64 rows of 32
+// floats (8 KB) at chunk (u * 10 + ks) * 512; chunk c of row r at slot
+// c ^ swz8(r) of its 128-byte line.  Tokens of the last tile past T get zeros.
 // ---------------------------------------------------------------------------
 template <int S>
 __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* __restrict__ part,
-                                                  const float* __restrict__ ssq, uint4* __restrict__ planes)
+                                                  const float* __restrict__ ssq, uint4* __restrict__ lo_tiled)
 {
     constexpr int Q = S / 4;  // splits per stream
-    const int idx = blockIdx.x * 256 + threadIdx.x;  // (token, chunk of 8 rank indices)
-    const int t = idx / (kRank / 8);
-    const int c8 = idx - t * (kRank / 8);
+    const int idx = blockIdx.x * 256 + threadIdx.x;  // (token, chunk of 4 rank indices)
+    const int t = idx / (kRank / 4);
+    const int c4 = idx - t * (kRank / 4);
     if (t >= Tpad)
         return;
-    float lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        lo[e] = 0.f;
+    float lo[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < T) {
-        float v[4][8];
+        float v[4][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            float ss = 0.f, sum[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sum[e] = 0.f;
+            float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
                 const int sg = Q * s + q;
                 ss += ssq[(size_t)sg * T + t];
-                const float* pp = part + ((size_t)sg * T + t) * kRank + 8 * c8;
-                const float4 a0 = *reinterpret_cast<const float4*>(pp), a1 = *reinterpret_cast<const float4*>(pp + 4);
-                const float pv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sum[e] += pv[e];
+                const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
+                sum[0] += a.x;
+                sum[1] += a.y;
+                sum[2] += a.z;
+                sum[3] += a.w;
             }
             const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < 4; ++e)
                 v[s][e] = sum[e] * rs;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 4; ++e)
             lo[e] = (v[0][e] + v[1][e]) + (v[2][e] + v[3][e]);
     }
-    uint32_t hi[8], mi[8], l3[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        split3(lo[e], hi[e], mi[e], l3[e]);
     const int tile = t / kTok, tl = t - tile * kTok;
-    const int ks = c8 >> 2, c = c8 & 3;
-    uint4* dst = planes + (size_t)(tile * kUpSteps + ks) * kLoBlock + panel_slot(tl, c);
-    dst[0] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-    dst[kPlaneChunks] = make_uint4(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16));
-    dst[2 * kPlaneChunks] = make_uint4(l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16));
+    const int ks = c4 >> 3, c = c4 & 7;
+    lo_tiled[(size_t)(tile * kUpSteps + ks) * kLoTile + 8 * tl + (c ^ swz8(tl))] =
+        make_uint4(__float_as_uint(lo[0]), __float_as_uint(lo[1]), __float_as_uint(lo[2]), __float_as_uint(lo[3]));
 }
 
 // ---------------------------------------------------------------------------
 // P3: up projection with the stream mix as its epilogue.  Workgroup b: XCD
 // x = b % 8, q = b / 8: token tile q / 5, column group x + 8 (q % 5) (64
-// columns).  Wave w computes columns c0 + 16 w .. +15 of all 4 streams for
-// all 64 tokens: MFMA A = W_up rows (one block per stream), B = lo planes (4
-// token blocks x 3 pieces); D then holds, in lane (n, g), token 16 tb + n and
-// columns 4 g .. 4 g + 3 of every stream, so the mix is per lane.
-// LDS stage (28 KB): W_up panel (256 rows: row 64 s + j = W_up row
-// s * 2560 + c0 + j, 16 KB), then the 3 lo panels (12 KB).
+// columns).  Wave w owns tokens 16 w .. 16 w + 15 of the tile and computes
+// all 64 columns of all 4 streams for them: MFMA A = W_up rows (4 column
+// blocks x 4 streams), B = lo of the wave's tokens, split in registers into
+// its three bf16 pieces.  D then holds, in lane (n, g), token 16 w + n and
+// columns 16 cb + 4 g .. +3 of every stream, so the mix is per lane.
+// LDS stage (24 KB): W_up panel (256 rows: row 64 s + j = W_up row
+// s * 2560 + c0 + j, 16 KB), then the tile's lo block of the step (8 KB).
+// Three stages, loaded two steps ahead.
 // ---------------------------------------------------------------------------
 constexpr int kUpWChunks = 4 * kUpCols * 4;      // 1024
-constexpr int kUpStage = kUpWChunks + kLoBlock;  // 1792 chunks
+constexpr int kUpStage = kUpWChunks + kLoTile;   // 1536 chunks
+constexpr int kUpSlots = 3;
+constexpr int kUpLoads = (kUpWChunks + kLoTile) / 64 / 4;  // wave instructions per stage and wave (6)
 
 template <bool HAS_P>
-__global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ planes,
+__global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* __restrict__ R,
                                                         const float* __restrict__ P,
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                                                         uint16_t* __restrict__ out_bf16,
                                                         uint16_t* __restrict__ out_fp16)
 {
-    __shared__ __align__(16) uint4 lds[2 * kUpStage];
+    __shared__ __align__(16) uint4 lds[kUpSlots * kUpStage];
 
     const int b = blockIdx.x;
     const int x = b & 7, q = b >> 3;
@@ -442,115 +463,174 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
 
-    // stage loads: wave instruction i (0..27): i < 16 fills W_up panel rows
-    // 16 i .. 16 i + 15 (lane l: row 16 i + l / 4, chunk (l & 3) ^ ((row >> 2) & 3));
-    // i >= 16 copies 1 KB of the lo block.  Wave w issues i = w + 4 k.
-    const int wchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    // stage loads: W_up panel instruction i (0..15) fills rows 16 i .. 16 i + 15
+    // (lane l: row 16 i + l / 4, chunk (l & 3) ^ ((row >> 1) & 3)); lo
+    // instruction i (0..7) copies 1 KB of the lo block.  Wave w issues W_up
+    // i = w + 4 k (k < 4) and lo i = w, w + 4.
+    const int wchunk = (lane & 3) ^ ((lane >> 3) & 3);
     const uint16_t* wu_lane[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int prow = 16 * (wave + 4 * k) + (lane >> 2);  // panel row = 64 s + j
         wu_lane[k] = W_up + (size_t)((prow >> 6) * kWidth + c0 + (prow & 63)) * kRank + 8 * wchunk;
     }
-    const uint4* lo_lane = planes + (size_t)tile * kUpSteps * kLoBlock + lane;
-    auto issue = [&](int ks, int stage) {
-        uint4* sb = lds + stage * kUpStage;
+    const uint4* lo_lane = lo_tiled + (size_t)tile * kUpSteps * kLoTile + lane;
+    auto issue = [&](int ks, int slot) {
+        uint4* sb = lds + slot * kUpStage;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             dma16(wu_lane[k] + kKs * ks, sb + 64 * (wave + 4 * k));
 #pragma unroll
-        for (int k = 4; k < 7; ++k) {
-            const int i = wave + 4 * k - 16;  // 1 KB piece of the lo block, 0..11
-            dma16(lo_lane + (size_t)ks * kLoBlock + 64 * i, sb + kUpWChunks + 64 * i);
-        }
+        for (int k = 0; k < 2; ++k)
+            dma16(lo_lane + (size_t)ks * kLoTile + 64 * (wave + 4 * k), sb + kUpWChunks + 64 * (wave + 4 * k));
     };
 
-    f32x4_t acc[4][4];  // [token block][stream]
+    f32x4_t acc[4][4];  // [column block][stream]
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc[tb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc[cb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const uint32_t lds0 = lds_addr(lds);
-    uint32_t aoff[4], boff[4];
+    // W_up operand of (stream s, column block cb): panel row 64 s + 16 cb + n,
+    // chunk g = this lane's slot in the first block plus 1 KB per block
+    const uint32_t aoff = 16 * panel_slot(n, g);
+    // lo of token 16 wave + n, floats 8 g .. 8 g + 7
+    const int lrow = 16 * wave + n;
+    const uint32_t lo_a = 16 * (kUpWChunks + 8 * lrow + ((2 * g) ^ swz8(lrow)));
+    const uint32_t lo_b = 16 * (kUpWChunks + 8 * lrow + ((2 * g + 1) ^ swz8(lrow)));
+    auto compute = [&](int slot) {
+        const uint32_t sb = lds0 + 16 * slot * kUpStage;
+        u32x4 lv[2];
+        lv[0] = ds_read16(sb + lo_a);
+        lv[1] = ds_read16(sb + lo_b);
+        u32x4 wa[8];
+        const uint32_t wb = sb + aoff;
+        wa[0] = ds_read16_off<0>(wb);
+        wa[1] = ds_read16_off<1024>(wb);
+        wa[2] = ds_read16_off<2048>(wb);
+        wa[3] = ds_read16_off<3072>(wb);
+        wa[4] = ds_read16_off<4096>(wb);
+        wa[5] = ds_read16_off<5120>(wb);
+        wa[6] = ds_read16_off<6144>(wb);
+        wa[7] = ds_read16_off<7168>(wb);
+        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+        asm volatile("" : "+v"(lv[0]), "+v"(lv[1]));
+        uint32_t hi[8], mi[8], l3[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        aoff[s] = 16 * panel_slot(64 * s + 16 * wave + n, g);
+        for (int e = 0; e < 8; ++e)
+            split3(__uint_as_float(lv[e >> 2][e & 3]), hi[e], mi[e], l3[e]);
+        u32x4 y[3];
+        y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
+        y[2] = u32x4{l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16)};
+        // streams 0-1 (column blocks 0..3) then streams 2-3: the second half's
+        // W_up operands are read while the first half's 24 MFMAs run
+        u32x4 wn[8];
+        wn[0] = ds_read16_off<8192>(wb);
+        wn[1] = ds_read16_off<9216>(wb);
+        wn[2] = ds_read16_off<10240>(wb);
+        wn[3] = ds_read16_off<11264>(wb);
+        wn[4] = ds_read16_off<12288>(wb);
+        wn[5] = ds_read16_off<13312>(wb);
+        wn[6] = ds_read16_off<14336>(wb);
+        wn[7] = ds_read16_off<15360>(wb);
+        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-        boff[tb] = 16 * (kUpWChunks + panel_slot(16 * tb + n, g));
-    auto compute = [&](int stage) {
-        const uint32_t sb = lds0 + 16 * stage * kUpStage;
-        u32x4 op[16];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            op[s] = ds_read16(sb + aoff[s]);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-                op[4 + 3 * tb + p] = ds_read16(sb + boff[tb] + 16 * kPlaneChunks * p);
-        lds_wait(op);
+        for (int k = 0; k < 8; ++k)
+            asm volatile("" : "+v"(wa[k]));
+        // panel block index k = 4 s + cb
 #pragma unroll
         for (int p = 2; p >= 0; --p)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int k = 0; k < 8; ++k)
+                acc[k & 3][k >> 2] = mfma16(wa[k], y[p], acc[k & 3][k >> 2]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc[tb][s] = mfma16(op[s], op[4 + 3 * tb + p], acc[tb][s]);
+        for (int k = 0; k < 8; ++k)
+            asm volatile("" : "+v"(wn[k]));
+#pragma unroll
+        for (int p = 2; p >= 0; --p)
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                acc[k & 3][2 + (k >> 2)] = mfma16(wn[k], y[p], acc[k & 3][2 + (k >> 2)]);
     };
 
-    issue(0, 0);
-    ring_barrier<0>();
-#pragma unroll 1
-    for (int ks = 0; ks < kUpSteps - 1; ++ks) {
-        issue(ks + 1, (ks + 1) & 1);
-        compute(ks & 1);
-        ring_barrier<0>();
-    }
-    compute((kUpSteps - 1) & 1);
+    // The epilogue's R: this lane's token, columns c0 + 16 cb + 4 g .. +3 of
+    // every stream (tokens past T re-read token T - 1 and store nothing).
+    // Its 16 loads are issued two steps before the end of the K loop, after
+    // the last stage's loads, and are counted in the waits that follow.
+    constexpr int kRLoads = 16;
+    const int t = t0 + lrow;
+    const int tr = t < T ? t : T - 1;
+    const float* rrow = R + (size_t)tr * kD + c0 + 4 * g;
+    float4 rv[4][4];  // [column block][stream]
 
-    // gated = up (identity epilogue); mixed = sum_s gated_s * R'_s, then images.
-    // Every R (and pending) load is issued before the first use (tokens past
-    // T re-read token T - 1 and store nothing).
-    const int c = c0 + 16 * wave + 4 * g;
-    float4 rv[4][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int t = t0 + 16 * tb + n < T ? t0 + 16 * tb + n : T - 1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            rv[tb][s] = *reinterpret_cast<const float4*>(R + (size_t)t * kD + s * kWidth + c);
+    // Step ks: stage ks + 2 is issued (the wait at the end of the step leaves
+    // exactly those loads in flight); the matrix cores run step ks.
+    issue(0, 0);
+    issue(1, 1);
+    ring_barrier<kUpLoads>();
+    int slot = 0;  // slot of step ks
+#pragma unroll 1
+    for (int ks = 0; ks < kUpSteps - 3; ++ks) {
+        issue(ks + 2, slot == 0 ? 2 : slot - 1);  // (ks + 2) % 3
+        compute(slot);
+        ring_barrier<kUpLoads>();
+        slot = slot == 2 ? 0 : slot + 1;
     }
-    if (HAS_P) {
+    issue(kUpSteps - 1, slot == 0 ? 2 : slot - 1);
+    order();
+    {
+        // Loads through a pointer the compiler cannot trace to the read-only
+        // argument: such loads count as ordinary memory accesses and stay
+        // between the surrounding asm statements, where the waits count them.
+        typedef __attribute__((address_space(1))) const f32x4_t gf32x4;  // global memory
+        gf32x4* rl = (gf32x4*)rrow;  // (an address-space cast: the loads stay global loads)
+        asm volatile("" : "+v"(rl));
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t = t0 + 16 * tb + n < T ? t0 + 16 * tb + n : T - 1;
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const float4 pv = *reinterpret_cast<const float4*>(P + (size_t)t * kD + s * kWidth + c);
-                rv[tb][s].x += pv.x;
-                rv[tb][s].y += pv.y;
-                rv[tb][s].z += pv.z;
-                rv[tb][s].w += pv.w;
+                const f32x4_t v = rl[(s * kWidth + 16 * cb) / 4];
+                rv[cb][s] = make_float4(v[0], v[1], v[2], v[3]);
             }
-        }
     }
+    compute(slot);
+    ring_barrier<kUpLoads + kRLoads>();
+    slot = slot == 2 ? 0 : slot + 1;
+    compute(slot);
+    ring_barrier<kRLoads>();
+    compute(slot == 2 ? 0 : slot + 1);
+
+    // gated = up (identity epilogue); mixed = sum_s gated_s * R'_s, then images.
+    if (HAS_P) {
+        const float* prow = P + (size_t)tr * kD + c0 + 4 * g;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int t = t0 + 16 * tb + n;
-        const float r[4][4] = {{rv[tb][0].x, rv[tb][0].y, rv[tb][0].z, rv[tb][0].w},
-                               {rv[tb][1].x, rv[tb][1].y, rv[tb][1].z, rv[tb][1].w},
-                               {rv[tb][2].x, rv[tb][2].y, rv[tb][2].z, rv[tb][2].w},
-                               {rv[tb][3].x, rv[tb][3].y, rv[tb][3].z, rv[tb][3].w}};
-        float m[4];
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            m[i] = (acc[tb][0][i] * r[0][i] + acc[tb][1][i] * r[1][i]) +
-                   (acc[tb][2][i] * r[2][i] + acc[tb][3][i] * r[3][i]);
-        if (t < T) {
-            const size_t o = (size_t)t * kWidth + c;
+            for (int s = 0; s < 4; ++s) {
+                const float4 pv = *reinterpret_cast<const float4*>(prow + s * kWidth + 16 * cb);
+                rv[cb][s].x += pv.x;
+                rv[cb][s].y += pv.y;
+                rv[cb][s].z += pv.z;
+                rv[cb][s].w += pv.w;
+            }
+    }
+    if (t < T) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
+                                   {rv[cb][1].x, rv[cb][1].y, rv[cb][1].z, rv[cb][1].w},
+                                   {rv[cb][2].x, rv[cb][2].y, rv[cb][2].z, rv[cb][2].w},
+                                   {rv[cb][3].x, rv[cb][3].y, rv[cb][3].z, rv[cb][3].w}};
+            float m[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = (acc[cb][0][i] * r[0][i] + acc[cb][1][i] * r[1][i]) +
+                       (acc[cb][2][i] * r[2][i] + acc[cb][3][i] * r[3][i]);
+            const size_t o = (size_t)t * kWidth + c0 + 16 * cb + 4 * g;
             *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
             uint32_t bh[4], hh[4];
 #pragma unroll
@@ -593,7 +673,7 @@ size_t part_slots(int chunk)
 size_t prefill_scratch_bytes(int chunk)
 {
     const size_t tpad = (size_t)tiles_of(chunk) * kTok;
-    return sizeof(float) * part_slots(chunk) * (kRank + 1) + sizeof(uint16_t) * 3 * tpad * kRank + 512;
+    return sizeof(float) * part_slots(chunk) * (kRank + 1) + sizeof(float) * tpad * kRank + 512;
 }
 
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
@@ -604,7 +684,7 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
     const size_t slots = part_slots(chunk);
     float* part = static_cast<float*>(scratch);  // [S][Tc][320]
     float* ssq = part + slots * kRank;             // [S][Tc]
-    uint4* planes = reinterpret_cast<uint4*>(      // tiled lo planes
+    uint4* planes = reinterpret_cast<uint4*>(      // tiled fp32 lo
         (reinterpret_cast<uintptr_t>(ssq + slots) + 255) & ~uintptr_t(255));
     for (int64_t c0 = 0; c0 < T; c0 += chunk) {
         const int Tc = (int)(T - c0 < chunk ? T - c0 : chunk);
@@ -628,7 +708,7 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         if (e != hipSuccess)
             return e;
         const int tiles = tiles_of(Tc);
-        const int items = tiles * kTok * (kRank / 8);
+        const int items = tiles * kTok * (kRank / 4);
         if (S == 8)
             hipLaunchKernelGGL(prefill_lo<8>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq, planes);
         else
