@@ -93,6 +93,10 @@ __device__ __forceinline__ u32x4 ds_read16_off(uint32_t addr)
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
     return v;
 }
+__device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
 // Waits for every LDS read of this wave; the values in `v` are then "produced
 // here", so no use of them moves above the wait.
 template <int N>
@@ -618,19 +622,41 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                 rv[cb][s].w += pv.w;
             }
     }
-    if (t < T) {
+    // The wave's 16 tokens x 64 columns of mixed go through 4 KB of LDS of its
+    // own (inside ring slot 1, which the last step does not read) so that
+    // every store instruction writes whole 128-byte lines: written in the MFMA
+    // layout (chunk 4 cb + g of row n at slot (4 cb + g) ^ n), read back as 4
+    // rows of 16 lanes x 16 bytes.
+    const uint32_t tb = lds0 + 16 * kUpStage + 4096 * wave;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
-                                   {rv[cb][1].x, rv[cb][1].y, rv[cb][1].z, rv[cb][1].w},
-                                   {rv[cb][2].x, rv[cb][2].y, rv[cb][2].z, rv[cb][2].w},
-                                   {rv[cb][3].x, rv[cb][3].y, rv[cb][3].z, rv[cb][3].w}};
-            float m[4];
+    for (int cb = 0; cb < 4; ++cb) {
+        const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
+                               {rv[cb][1].x, rv[cb][1].y, rv[cb][1].z, rv[cb][1].w},
+                               {rv[cb][2].x, rv[cb][2].y, rv[cb][2].z, rv[cb][2].w},
+                               {rv[cb][3].x, rv[cb][3].y, rv[cb][3].z, rv[cb][3].w}};
+        float m[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                m[i] = (acc[cb][0][i] * r[0][i] + acc[cb][1][i] * r[1][i]) +
-                       (acc[cb][2][i] * r[2][i] + acc[cb][3][i] * r[3][i]);
-            const size_t o = (size_t)t * kWidth + c0 + 16 * cb + 4 * g;
+        for (int i = 0; i < 4; ++i)
+            m[i] = (acc[cb][0][i] * r[0][i] + acc[cb][1][i] * r[1][i]) +
+                   (acc[cb][2][i] * r[2][i] + acc[cb][3][i] * r[3][i]);
+        ds_write16(tb + 256 * n + 16 * ((4 * cb + g) ^ n),
+                   u32x4{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])});
+    }
+    u32x4 mv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = (lane >> 4) + 4 * k, ch = lane & 15;
+        mv[k] = ds_read16(tb + 256 * row + 16 * (ch ^ row));
+    }
+    lds_wait(mv);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = (lane >> 4) + 4 * k, ch = lane & 15;
+        const int tt = t0 + 16 * wave + row;
+        if (tt < T) {
+            const size_t o = (size_t)tt * kWidth + c0 + 4 * ch;
+            const float m[4] = {__uint_as_float(mv[k][0]), __uint_as_float(mv[k][1]), __uint_as_float(mv[k][2]),
+                                __uint_as_float(mv[k][3])};
             *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
             uint32_t bh[4], hh[4];
 #pragma unroll
