@@ -155,23 +155,28 @@ constexpr int kLoTile = kTok * 8;              // fp32 lo of one (token tile, K 
 // P1: down projection partials and sums of squares.  Workgroup b: split
 // b % S of width 10240 / S (stream halves or quarters; with S = 8 the split is
 // the XCD's, with S = 16 each XCD owns two), token tile b / S of 128 tokens.
-// Wave w owns tokens 16 w .. 16 w + 15 of the tile and computes all 320 rows
-// for them: MFMA A = W_down rows (20 blocks of 16), B = that wave's y = R' *
-// w_norm, split in registers into its three bf16 pieces (each wave converts
-// only its own tokens, so no y panel is shared through LDS).
-// Everything reaches LDS by direct loads: the W_down panel of a step one step
-// ahead (2 slots), raw R and pending three steps ahead (3 slots), and the
-// split's w_norm once.  No loaded value lives in registers across a step;
-// the converted y of the next step does (it is computed while the matrix
-// cores run the current one).
-// Raw rows are 32 floats (8 chunks of 16 bytes); chunk c of row r sits at slot
-// c ^ swz(r) of its 128-byte line, so 16 lanes reading one chunk of 16 rows
-// hit distinct bank groups.
+// The 12 waves specialise (wave w runs on SIMD w % 4, so each SIMD holds two
+// matrix waves and one producer): the vector work of the producers overlaps
+// the matrix cores instead of adding to them, and two matrix waves per SIMD
+// keep its matrix core issuing.
+//  * matrix waves 0-7: wave m computes all 320 rows for tokens 16 m .. +15:
+//    MFMA A = W_down rows (20 blocks of 16), B = the y panels of its token
+//    block; it reads LDS and issues MFMAs only.
+//  * producer waves 8-11: issue every load (the W_down panel of a step one step
+//    ahead, raw R and pending three steps ahead, the split's w_norm once) and
+//    turn the raw activations of the next step into y = R' * w_norm, split
+//    exactly into three bf16 panels, with the tokens' sums of squares.
+// LDS: 2 W_down slots (20 KB), 2 y slots (3 panels of 128 rows, 24 KB), raw
+// slots of 128 rows x 32 floats for R and pending (16 KB each; 3 slots, or 2
+// with pending, which then arrive two steps ahead), w_norm.
+// Raw rows: chunk c of row r at slot c ^ swz8(r) of its 128-byte line.
 // ---------------------------------------------------------------------------
 constexpr int kDnTok = 128;
-constexpr int kDnWaves = 8;
+constexpr int kDnWaves = 12;
+constexpr int kDnMatrixWaves = 8;
 constexpr int kDnWChunks = kRank * 4;           // W_down panel: 1280 chunks (20 KB)
 constexpr int kDnRawChunks = kDnTok * 8;        // raw R (or pending) of a step: 1024 chunks (16 KB)
+constexpr int kDnYChunks = 3 * kDnTok * 4;      // y: 3 panels of 128 rows x 4 chunks (24 KB)
 
 template <int S, bool HAS_P>
 __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float* __restrict__ R,
@@ -182,16 +187,19 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
 {
     constexpr int SW = kD / S;              // columns of a split
     constexpr int NS = SW / kKs;            // K steps
-    constexpr int kRawSlots = 3;
+    constexpr int RS = HAS_P ? 2 : 3;       // raw slots (pending doubles each; 3 would not fit in LDS)
     constexpr int kRawSet = (HAS_P ? 2 : 1) * kDnRawChunks;
-    // LDS (chunks): 2 W_down slots, 3 raw slots (R, then pending), w_norm
     constexpr int kWOff = 0;
-    constexpr int kRawOff = 2 * kDnWChunks;
-    constexpr int kNormOff = kRawOff + kRawSlots * kRawSet;
+    constexpr int kYOff = 2 * kDnWChunks;
+    constexpr int kRawOff = kYOff + 2 * kDnYChunks;
+    constexpr int kNormOff = kRawOff + RS * kRawSet;
     constexpr int kLdsChunks = kNormOff + SW / 4;
-    // raw-load wave instructions per step and wave (16 per array, 8 waves)
-    constexpr int kRawLoads = (HAS_P ? 2 : 1) * (kDnRawChunks / 64) / kDnWaves;
-    static_assert(kDnRawChunks % (64 * kDnWaves) == 0 && SW % kKs == 0 && NS >= 3, "tiling");
+    // raw-load wave instructions per step and producer wave (16 per array, 4
+    // waves), and how many of them a step's closing wait may leave in flight
+    constexpr int kRawLoads = (HAS_P ? 2 : 1) * (kDnRawChunks / 64) / 4;
+    constexpr int kFly = RS == 3 ? kRawLoads : 0;
+    static_assert(SW % kKs == 0 && NS >= 4, "tiling");
+    static_assert(kLdsChunks * 16 <= 160 * 1024, "LDS");
     __shared__ __align__(16) uint4 lds[kLdsChunks];
 
     const int b = blockIdx.x;
@@ -200,100 +208,156 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
     const int kbase = sig * SW;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, g = lane >> 4;
     const uint32_t lds0 = lds_addr(lds);
 
-    // W_down panel: wave instruction q (0..19) fills panel rows 16 q .. 16 q + 15
-    // (lane l: row 16 q + l / 4, chunk (l & 3) ^ ((row >> 1) & 3)); wave w
-    // issues q = w, w + 8 and (w < 4) w + 16.
-    const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
-    const uint16_t* wd_lane = W_down + (size_t)(lane >> 2) * kD + kbase + 8 * dchunk;
-    // raw R / pending: wave instruction q (0..15) fills rows 8 q .. 8 q + 7 (lane
-    // l: row 8 q + l / 8, chunk (l & 7) ^ swz8(row)); wave w issues q = w, w + 8.
-    // Rows past T re-read row T - 1 (their results are never stored).
-    const float* rraw[2];
-    const float* praw[2];
+    if (wave >= kDnMatrixWaves) {
+        // =========================== producer ===========================
+        const int pw = wave - kDnMatrixWaves;
+        // W_down panel: wave instruction q (0..19) fills panel rows 16 q .. +15
+        // (lane l: row 16 q + l / 4, chunk (l & 3) ^ ((row >> 1) & 3)); wave pw
+        // issues q = pw + 4 k, k < 5.
+        const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+        const uint16_t* wd_lane = W_down + (size_t)(lane >> 2) * kD + kbase + 8 * dchunk;
+        // raw: wave instruction q (0..15) fills rows 8 q .. 8 q + 7 (lane l: row
+        // 8 q + l / 8, chunk (l & 7) ^ swz8(row)); wave pw issues q = pw + 4 k,
+        // k < 4.  Rows past T re-read row T - 1 (their results are never stored).
+        const float* rraw[4];
+        const float* praw[4];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int q = wave + 8 * k;
-        const int row = 8 * q + (lane >> 3);
-        const int tr = t0 + row < T ? t0 + row : T - 1;
-        const int ch = (lane & 7) ^ swz8(row);
-        rraw[k] = R + (size_t)tr * kD + kbase + 4 * ch;
-        praw[k] = HAS_P ? P + (size_t)tr * kD + kbase + 4 * ch : nullptr;
+        for (int k = 0; k < 4; ++k) {
+            const int q = pw + 4 * k;
+            const int row = 8 * q + (lane >> 3);
+            const int tr = t0 + row < T ? t0 + row : T - 1;
+            const int ch = (lane & 7) ^ swz8(row);
+            rraw[k] = R + (size_t)tr * kD + kbase + 4 * ch;
+            praw[k] = HAS_P ? P + (size_t)tr * kD + kbase + 4 * ch : nullptr;
+        }
+        auto issue_w = [&](int ks) {
+#pragma unroll
+            for (int k = 0; k < 5; ++k) {
+                const int q = pw + 4 * k;
+                dma16(wd_lane + (size_t)(16 * q) * kD + kKs * ks, lds + kWOff + (ks & 1) * kDnWChunks + 64 * q);
+            }
+        };
+        auto issue_raw = [&](int ks) {
+            const int slot = ks % RS;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int q = pw + 4 * k;
+                dma16(rraw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + 64 * q);
+                if (HAS_P)
+                    dma16(praw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + kDnRawChunks + 64 * q);
+            }
+        };
+        // conversion role: token row cr = (64 pw + lane) / 2, columns 16 h .. 16 h + 15
+        const int cr = (64 * pw + lane) >> 1, h = lane & 1;
+        const bool tok_ok = t0 + cr < T;
+        float ssacc = 0.f;
+        auto convert = [&](int ks) {
+            const uint32_t rb = lds0 + 16 * (kRawOff + (ks % RS) * kRawSet + 8 * cr);
+            u32x4 v[12];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                v[c] = ds_read16(rb + 16 * ((4 * h + c) ^ swz8(cr)));
+                if (HAS_P)
+                    v[4 + c] = ds_read16(rb + 16 * kDnRawChunks + 16 * ((4 * h + c) ^ swz8(cr)));
+                v[8 + c] = ds_read16(lds0 + 16 * (kNormOff + 8 * ks + 4 * h + c));  // w_norm[32 ks + 16 h + 4 c ..]
+            }
+            lds_wait(v);
+            uint32_t hi[16], mi[16], lo[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = __uint_as_float(v[e >> 2][e & 3]);
+                if (HAS_P)
+                    x += __uint_as_float(v[4 + (e >> 2)][e & 3]);
+                ssacc += x * x;
+                split3(x * __uint_as_float(v[8 + (e >> 2)][e & 3]), hi[e], mi[e], lo[e]);
+            }
+            // panel chunks 2 h and 2 h + 1 of row cr, in each of the 3 panels
+            const uint32_t yb = lds0 + 16 * (kYOff + (ks & 1) * kDnYChunks);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const uint32_t a = yb + 16 * panel_slot(cr, 2 * h + c);
+                const int e = 8 * c;
+                ds_write16(a, u32x4{hi[e] | (hi[e + 1] << 16), hi[e + 2] | (hi[e + 3] << 16),
+                                    hi[e + 4] | (hi[e + 5] << 16), hi[e + 6] | (hi[e + 7] << 16)});
+                ds_write16(a + 16 * kDnTok * 4, u32x4{mi[e] | (mi[e + 1] << 16), mi[e + 2] | (mi[e + 3] << 16),
+                                                      mi[e + 4] | (mi[e + 5] << 16), mi[e + 6] | (mi[e + 7] << 16)});
+                ds_write16(a + 32 * kDnTok * 4, u32x4{lo[e] | (lo[e + 1] << 16), lo[e + 2] | (lo[e + 3] << 16),
+                                                      lo[e + 4] | (lo[e + 5] << 16), lo[e + 6] | (lo[e + 7] << 16)});
+            }
+        };
+        // Schedule: raw of step k is issued at step k - RS (prologue for the
+        // first RS steps), W_down of step k at step k - 1; step k's raw is
+        // converted during step k - 1.  With 3 raw slots the wait ending step j
+        // may leave the raw issued at step j in flight (it is converted two
+        // steps later); with 2 slots it is converted at the next step and every
+        // wait drains.
+        issue_w(0);
+        if (64 * pw + lane < SW / 4)  // the split's w_norm: SW / 4 chunks, at most 8 wave instructions
+            dma16(w_norm + kbase + 4 * (64 * pw + lane), lds + kNormOff + 64 * pw);
+        if (64 * (pw + 4) + lane < SW / 4)
+            dma16(w_norm + kbase + 4 * (64 * (pw + 4) + lane), lds + kNormOff + 64 * (pw + 4));
+#pragma unroll
+        for (int k = 0; k < RS - 1; ++k)
+            issue_raw(k);
+        order();
+        issue_raw(RS - 1);
+        ring_barrier<kRawLoads>();      // B0: W(0), w_norm, raw(0..RS-2) landed
+        convert(0);
+        ring_barrier<kFly>();           // B1: y(0) staged (and raw(1) landed when RS == 2)
+#pragma unroll 1
+        for (int j = 0; j < NS; ++j) {  // barrier B(j + 2) ends step j
+            if (j + 1 < NS)
+                issue_w(j + 1);
+            order();
+            const bool more = j + RS < NS;
+            if (more)
+                issue_raw(j + RS);       // into the slot of step j (converted during step j - 1)
+            if (j + 1 < NS)
+                convert(j + 1);
+            if (more)
+                ring_barrier<kFly>();
+            else
+                ring_barrier<0>();
+        }
+        // sums of squares: lanes 2 i and 2 i + 1 hold the two halves of token cr
+        const float ss = ssacc + __shfl_xor(ssacc, 1);
+        if (h == 0 && tok_ok)
+            ssq[(size_t)sig * T + t0 + cr] = ss;
+        return;
     }
-    auto issue_w = [&](int ks, int slot) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int q = wave + 8 * k;
-            if (k < 2 || wave < 4)
-                dma16(wd_lane + (size_t)(16 * q) * kD + kKs * ks, lds + kWOff + slot * kDnWChunks + 64 * q);
-        }
-    };
-    auto issue_raw = [&](int ks, int slot) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int q = wave + 8 * k;
-            dma16(rraw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + 64 * q);
-            if (HAS_P)
-                dma16(praw[k] + kKs * ks, lds + kRawOff + slot * kRawSet + kDnRawChunks + 64 * q);
-        }
-    };
 
+    // ============================= matrix =============================
+    const int m = wave;
+    const int n = lane & 15, g = lane >> 4;
     f32x4_t acc[20];
 #pragma unroll
     for (int jb = 0; jb < 20; ++jb)
         acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ssacc = 0.f;
-
-    // this lane's B operand: token 16 wave + n, columns 8 g .. 8 g + 7 of the step
-    const int trow = 16 * wave + n;
-    const bool tok_ok = t0 + trow < T;
-    const uint32_t raw_a = 16 * (trow * 8 + ((2 * g) ^ swz8(trow)));
-    const uint32_t raw_b = 16 * (trow * 8 + ((2 * g + 1) ^ swz8(trow)));
-    // W_down operand of row block jb: panel slot of row 16 jb + n, chunk g,
-    // i.e. this lane's slot in block 0 plus 1 KB per block
+    // operands: W_down row block jb = this lane's slot in block 0 plus 1 KB per
+    // block; y of token 16 m + n, chunk g, panel p
     const uint32_t aoff = 16 * panel_slot(n, g);
-
-    // y = R' * w_norm of step ks for this lane, split into its three bf16
-    // pieces (and the square sum accumulated), from raw slot rslot
-    auto convert = [&](int ks, int rslot, u32x4 (&y)[3]) {
-        const uint32_t rb = lds0 + 16 * (kRawOff + rslot * kRawSet);
-        u32x4 raw[6];
-        raw[0] = ds_read16(rb + raw_a);
-        raw[1] = ds_read16(rb + raw_b);
-        if (HAS_P) {
-            raw[2] = ds_read16(rb + 16 * kDnRawChunks + raw_a);
-            raw[3] = ds_read16(rb + 16 * kDnRawChunks + raw_b);
-        }
-        const uint32_t nb = lds0 + 16 * (kNormOff + 2 * (4 * ks + g));  // w_norm[32 ks + 8 g ..]
-        raw[4] = ds_read16(nb);
-        raw[5] = ds_read16(nb + 16);
-        lds_wait(raw);
-        uint32_t hi[8], mi[8], lo[8];
+    const uint32_t yoff = 16 * panel_slot(16 * m + n, g);
+    auto compute = [&](int ks) {
+        const uint32_t wb = lds0 + 16 * (kWOff + (ks & 1) * kDnWChunks) + aoff;
+        const uint32_t yb = lds0 + 16 * (kYOff + (ks & 1) * kDnYChunks);
+        u32x4 y[3];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = __uint_as_float(raw[e >> 2][e & 3]);
-            if (HAS_P)
-                x += __uint_as_float(raw[2 + (e >> 2)][e & 3]);
-            x = tok_ok ? x : 0.f;
-            ssacc += x * x;
-            split3(x * __uint_as_float(raw[4 + (e >> 2)][e & 3]), hi[e], mi[e], lo[e]);
-        }
-        y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-        y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
-        y[2] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
-    };
-    // The 60 MFMAs of a step on y: 4 groups of 5 row blocks, the next group's
-    // W_down operands read while this group's 15 MFMAs run.
-    auto mma = [&](int wslot, const u32x4 (&y)[3]) {
-        const uint32_t wb = lds0 + 16 * (kWOff + wslot * kDnWChunks) + aoff;
+        for (int p = 0; p < 3; ++p)
+            y[p] = ds_read16(yb + yoff + 16 * kDnTok * 4 * p);
         u32x4 wa[5];
         wa[0] = ds_read16_off<0>(wb);
         wa[1] = ds_read16_off<1024>(wb);
         wa[2] = ds_read16_off<2048>(wb);
         wa[3] = ds_read16_off<3072>(wb);
         wa[4] = ds_read16_off<4096>(wb);
+        asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory");
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+            asm volatile("" : "+v"(y[p]));
+        // 4 groups of 5 row blocks: the next group's operands are read while
+        // this group's 15 MFMAs run
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
             u32x4 wn[5];
@@ -323,64 +387,21 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
             }
         }
     };
-
-    // Step ks: W_down of step ks + 1 is issued, then the raw activations of
-    // step ks + 3 (the wait at the end of the step leaves exactly those in
-    // flight); the matrix cores run step ks on y, computed during step ks - 1,
-    // while step ks + 1's raw slot (landed by the previous wait) is turned
-    // into the next y.  Raw slot of step k: k % 3 (step k + 3 reuses step k's
-    // slot, converted during step k - 1).
-    issue_w(0, 0);
-    if (64 * wave + lane < SW / 4)  // the split's w_norm, SW / 4 chunks
-        dma16(w_norm + kbase + 4 * (64 * wave + lane), lds + kNormOff + 64 * wave);
-    issue_raw(0, 0);
-    issue_raw(1, 1);
-    order();
-    issue_raw(2, 2);
-    ring_barrier<kRawLoads>();
-    u32x4 ycur[3], ynext[3];
-    convert(0, 0, ycur);
-    ring_barrier<kRawLoads>();  // every wave is done with raw slot 0 before step 0 refills it
-    int rs1 = 1;  // raw slot of step ks + 1
+    ring_barrier<0>();  // B0
+    ring_barrier<0>();  // B1: y(0) and W(0) in LDS
 #pragma unroll 1
-    for (int ks = 0; ks < NS - 3; ++ks) {
-        issue_w(ks + 1, (ks + 1) & 1);
-        order();
-        issue_raw(ks + 3, rs1 == 0 ? 2 : rs1 - 1);  // (ks + 3) % 3 == ks % 3
-        convert(ks + 1, rs1, ynext);
-        mma(ks & 1, ycur);
-        ring_barrier<kRawLoads>();
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-            ycur[p] = ynext[p];
-        rs1 = rs1 == 2 ? 0 : rs1 + 1;
+    for (int j = 0; j < NS; ++j) {
+        compute(j);
+        ring_barrier<0>();  // B(j + 2)
     }
-#pragma unroll
-    for (int ks = NS - 3; ks < NS - 1; ++ks) {  // nothing more to load after step NS - 1's raw slot
-        issue_w(ks + 1, (ks + 1) & 1);
-        convert(ks + 1, rs1, ynext);
-        mma(ks & 1, ycur);
-        ring_barrier<0>();
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-            ycur[p] = ynext[p];
-        rs1 = rs1 == 2 ? 0 : rs1 + 1;
-    }
-    mma((NS - 1) & 1, ycur);
-
-    // partials: lane holds token t0 + 16 wave + n, rows 16 jb + 4 g .. +3
-    const int t = t0 + trow;
-    if (tok_ok) {
+    // partials: lane holds token t0 + 16 m + n, rows 16 jb + 4 g .. +3
+    const int t = t0 + 16 * m + n;
+    if (t < T) {
         float* dst = part + ((size_t)sig * T + t) * kRank + 4 * g;
 #pragma unroll
         for (int jb = 0; jb < 20; ++jb)
             *reinterpret_cast<f32x4_t*>(dst + 16 * jb) = acc[jb];
     }
-    // sum of squares of the token: lanes n, n + 16, n + 32, n + 48
-    const float s1 = ssacc + __shfl_xor(ssacc, 16);
-    const float s2 = s1 + __shfl_xor(s1, 32);
-    if (g == 0 && tok_ok)
-        ssq[(size_t)sig * T + t] = s2;
 }
 
 // ---------------------------------------------------------------------------
