@@ -168,31 +168,56 @@ def main():
         traffic = measured[0]  # HBM bytes per launch, sweep average
 
     prefill = None
+    prefill_all = None
     if not args.no_prefill:
         from hyper_connection_residual_amd import workloads as wl
-        inp = wl.config_inputs(4)
-        R = torch.from_numpy(inp.R).cuda()
-        w_norm = torch.from_numpy(inp.w_norm).cuda()
-        Wd = torch.from_numpy(inp.W_down.view(np.int16)).cuda()
-        Wu = torch.from_numpy(inp.W_up.view(np.int16)).cuda()
-        T = inp.T
-        o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
-             torch.empty((T, 2560), dtype=torch.int16, device=dev),
-             torch.empty((T, 2560), dtype=torch.int16, device=dev))
-        for _ in range(3):
-            binding.hc_read(T, R, None, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        a.record(stream)
-        for _ in range(reps):
-            binding.hc_read(T, R, None, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        prefill = {"T": T, "ms_per_read": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
-        print("# prefill T=8192: %.4f ms per read" % ms, file=sys.stderr, flush=True)
-        del R, Wd, Wu, o
+
+        def time_wide(T, R, P, w_norm, Wd, Wu, reps):
+            o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
+                 torch.empty((T, 2560), dtype=torch.int16, device=dev),
+                 torch.empty((T, 2560), dtype=torch.int16, device=dev))
+            for _ in range(3):
+                binding.hc_read(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                binding.hc_read(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            return {"T": T, "pending": P is not None, "ms_per_read": round(ms, 4),
+                    "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+        prefill_all = {}
+        # configs 3 and 4: the seeded generator (outlier channels, no pending)
+        for c in (3, 4):
+            inp = wl.config_inputs(c)
+            R = torch.from_numpy(inp.R).cuda()
+            w_norm = torch.from_numpy(inp.w_norm).cuda()
+            Wd = torch.from_numpy(inp.W_down.view(np.int16)).cuda()
+            Wu = torch.from_numpy(inp.W_up.view(np.int16)).cuda()
+            r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 20 if inp.T <= 2048 else 10)
+            prefill_all["T%d" % inp.T] = r
+            print("# prefill T=%d: %.4f ms per read" % (inp.T, r["ms_per_read"]), file=sys.stderr, flush=True)
+            del R
+        # config 5 (T = 32768 with pending): the same distributions drawn on the
+        # device (R ~ Student-t(4) / sqrt(2), pending ~ N(0, 0.05)); the read's
+        # time does not depend on the values, and the seeded CPU draw of 2.7 GB
+        # takes ~40 s
+        g = torch.Generator(device=dev)
+        g.manual_seed(4)
+        T5 = 32768
+        z = torch.randn((T5, 4, 2560), device=dev, generator=g)
+        chi = torch.distributions.Chi2(torch.tensor(4.0, device=dev)).sample((T5, 4, 2560))
+        R5 = (z / torch.sqrt(chi / 4.0) / np.sqrt(2.0)).contiguous()
+        del z, chi
+        P5 = (0.05 * torch.randn((T5, 4, 2560), device=dev, generator=g)).contiguous()
+        r = time_wide(T5, R5, P5, w_norm, Wd, Wu, 3)
+        prefill_all["T32768_pending"] = r
+        print("# prefill T=32768 with pending: %.4f ms per read" % r["ms_per_read"], file=sys.stderr, flush=True)
+        del R5, P5, Wd, Wu
+        prefill = prefill_all["T8192"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,6 +260,7 @@ def main():
                    "streams": 4, "width": 2560, "rank": 320},
         "us_per_read": us_per_read,
         "prefill_T8192": prefill,
+        "prefill": prefill_all,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
