@@ -9,8 +9,9 @@ more than the 256 MB Infinity Cache) rotated per read so every read streams its
 on the next weight set).  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` = weight bytes streamed per second over the
-timed sweeps (GB/s); per-T microseconds per read and the T = 8192 prefill read
-time are reported beside it.  The roofline object describes the short-window
+timed sweeps (GB/s), one hc_read call per read; the same sweeps replayed from
+captured HIP graphs (one graph per step) are reported under `graph`.  Per-T
+microseconds per read and the prefill read times are reported beside it.  The roofline object describes the short-window
 kernel; the CPU baseline is the plain oracle on the host.
 """
 from __future__ import annotations
@@ -93,63 +94,95 @@ def main():
                 torch.empty((T, 2560), dtype=torch.int16, device=dev)) for T in TS}
     print("# inputs ready in %.1f s" % (time.time() - t_gen), file=sys.stderr, flush=True)
 
-    counter = [0]
-
-    def one_read(T):
-        m = counter[0] % N_SETS
-        counter[0] += 1
+    def read_on(T, m, s):
         ws = sets[m]
         R, P = acts[(T, m)]
         o = outs[T]
-        st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2],
-                             stream.cuda_stream)
+        st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2], s.cuda_stream)
         if st != 0:
             raise binding.HCError(st, "hc_read")
 
-    def step():
-        for T in TS:
-            one_read(T)
+    # read number i of a run uses weight set i mod 48: step k covers sets
+    # 8 k .. 8 k + 7 (mod 48), so 6 consecutive steps touch every set once
+    n_pos = N_SETS // len(TS)
 
-    # warmup, then exactly K timed steps bracketed by synchronisation
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-    n_reads = args.steps * len(TS)
-    weight_gbps = n_reads * WEIGHT_BYTES / (ms_total * 1e-3) / 1e9
-    print("# timed %d steps: %.3f ms/step (event), wall %.3f s" % (args.steps, ms_per_step, wall),
-          file=sys.stderr, flush=True)
+    def eager_step(k):
+        for i, T in enumerate(TS):
+            read_on(T, (len(TS) * k + i) % N_SETS, stream)
 
-    # per-T microseconds per read (300 reads each, rotating the weight sets)
-    us_per_read = {}
-    for T in TS:
-        for _ in range(10):
-            one_read(T)
+    def time_region(s, body, n):
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(300):
-            one_read(T)
-        b.record(stream)
+        a.record(s)
+        with torch.cuda.stream(s):
+            for k in range(n):
+                body(k)
+        b.record(s)
         torch.cuda.synchronize()
-        us_per_read[str(T)] = round(a.elapsed_time(b) * 1e3 / 300, 3)
-    print("# us per read by T: %s" % us_per_read, file=sys.stderr, flush=True)
+        return a.elapsed_time(b)
+
+    # ---- eager: one hc_read call per read, back to back on one stream
+    for k in range(args.warmup):
+        eager_step(k)
+    t0 = time.perf_counter()
+    ms_eager = time_region(stream, eager_step, args.steps)
+    print("# eager: %d steps, %.3f ms/step (event), wall %.3f s"
+          % (args.steps, ms_eager / args.steps, time.perf_counter() - t0), file=sys.stderr, flush=True)
+    us_eager = {}
+    for T in TS:
+        for m in range(10):
+            read_on(T, m, stream)
+        ms = time_region(stream, lambda k, T=T: read_on(T, k % N_SETS, stream), 300)
+        us_eager[str(T)] = round(ms * 1e3 / 300, 3)
+    print("# eager us per read by T: %s" % us_eager, file=sys.stderr, flush=True)
+
+    # ---- HIP graphs: each step position of the rotation captured once (8
+    # reads per graph) and replayed; the same reads, inputs and outputs as the
+    # eager run.  Scratch of the capture stream is created eagerly first.
+    gstream = torch.cuda.Stream()
+    with torch.cuda.stream(gstream):
+        for T in TS:
+            read_on(T, 0, gstream)
+    torch.cuda.synchronize()
+    step_graphs = []
+    for j in range(n_pos):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for i, T in enumerate(TS):
+                read_on(T, (len(TS) * j + i) % N_SETS, gstream)
+        step_graphs.append(g)
+    for k in range(args.warmup):
+        with torch.cuda.stream(gstream):
+            step_graphs[k % n_pos].replay()
+    t0 = time.perf_counter()
+    ms_graph = time_region(gstream, lambda k: step_graphs[k % n_pos].replay(), args.steps)
+    print("# graph: %d steps, %.3f ms/step (event), wall %.3f s"
+          % (args.steps, ms_graph / args.steps, time.perf_counter() - t0), file=sys.stderr, flush=True)
+    us_graph = {}
+    for T in TS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for m in range(N_SETS):
+                read_on(T, m, gstream)
+        with torch.cuda.stream(gstream):
+            g.replay()
+        ms = time_region(gstream, lambda k, g=g: g.replay(), 6)
+        us_graph[str(T)] = round(ms * 1e3 / (6 * N_SETS), 3)
+        del g
+    print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
+    del step_graphs
+
+    ms_per_step = ms_eager / args.steps
+    n_reads = args.steps * len(TS)
+    weight_gbps = n_reads * WEIGHT_BYTES / (ms_eager * 1e-3) / 1e9
+    us_per_read = us_eager
 
     # the short-window kernel's roofline over the sweep: algorithmic bytes per
     # launch (weights + each token's R, pending and outputs) / event-timed
-    # average launch duration (back-to-back launches on this stream)
+    # average launch duration (back-to-back launches on one stream)
     alg_bytes_per_step = sum(WEIGHT_BYTES + T * TOKEN_BYTES_P for T in TS)
     achieved = alg_bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    timeouts = binding.hc_timeouts(stream)
+    timeouts = binding.hc_timeouts(stream) + binding.hc_timeouts(gstream)
     if timeouts:
         print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
 
@@ -259,6 +292,8 @@ def main():
                    "T": TS, "weight_sets": N_SETS, "reads_per_step": len(TS),
                    "streams": 4, "width": 2560, "rank": 320},
         "us_per_read": us_per_read,
+        "graph": {"value": round(n_reads * WEIGHT_BYTES / (ms_graph * 1e-3) / 1e9, 2),
+                  "ms_per_step": round(ms_graph / args.steps, 5), "us_per_read": us_graph},
         "prefill_T8192": prefill,
         "prefill": prefill_all,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,

@@ -40,9 +40,10 @@
 //   workgroups reduce the 16 partials of 3 rows each through the XCD's L2
 //   (hop 1) and publish lo device-wide; every up workgroup gathers all of lo
 //   (hop 2).  Hand-off words are 64 bits holding the payload and the launch's
-//   generation number, written once with one store; a consumer polls one
-//   sentinel word per producer (its last store), then reads the data once and
-//   re-reads only words whose tag is still old.  Every workgroup counts its
+//   generation number, written once with one store; a consumer polls the data
+//   words themselves (device-coherent loads, which see a write-through store
+//   from another XCD even when they started polling before it), with every
+//   load of a polling round in flight at once.  Every workgroup counts its
 //   launches in its own slot, so all of them agree on the generation without
 //   host involvement (the launch is graph-capture safe).  Every wait is
 //   bounded.
@@ -107,11 +108,11 @@ __host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
 // LDS bytes per role: the weight tile, then the role's planes
 constexpr size_t down_lds(int T)
 {
-    return 16 * kTileChunks + 2 * 3 * T * kYRow + 4 * T * kStageItems + 3 * 64 * 16;
+    return 16 * kTileChunks + 2 * 3 * T * kYRow + 4 * T * kStageItems + 6 * 2 * 64 * 16;
 }
 constexpr size_t up_lds(int T)
 {
-    return 16 * kTileChunks + 2 * 3 * T * kLoRow + 4 * T * kUpRows;
+    return 16 * kTileChunks + 2 * 3 * T * kLoRow + 4 * T * kUpRows + (kDecUpCols / 4) * 2 * 64 * 16;
 }
 constexpr size_t lds_bytes(int T)
 {
@@ -136,6 +137,32 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
     hi = hb >> 16;
     mid = mb >> 16;
     lo3 = __float_as_uint(r2) >> 16;
+}
+
+// Short-window MFMA blocks put (piece, token) pairs on the 16 A rows: row
+// p T + t holds piece p (0 hi, 1 mid, 2 lo3) of token t.  kChains: MFMA chains
+// per block (1 when all 3 T rows fit, else 2: pieces 0-1, then piece 2 on rows
+// 0..T-1).  kPackRows: the A rows chain 0 carries.
+template <int T>
+constexpr int kChains = 3 * T <= 16 ? 1 : 2;
+template <int T>
+constexpr int kPackRows = kChains<T> == 1 ? 3 * T : 2 * T;
+
+// Product-block element (piece p, token t; column = the lane's n) of block w,
+// from blocks stored in LDS as [block][chain][64 lanes] f32x4 (the MFMA's own
+// register layout: row i of column n sits in lane n + 16 (i / 4), element i % 4).
+template <int T>
+__device__ __forceinline__ float packed_at(const float* cf, int w, int p, int t, int n)
+{
+    const int c = (kChains<T> == 2 && p == 2) ? 1 : 0;
+    const int i = c ? t : p * T + t;
+    return cf[((w * kChains<T> + c) * 64 + n + 16 * (i >> 2)) * 4 + (i & 3)];
+}
+// The three pieces' products of token t summed: hi + (mid + lo3).
+template <int T>
+__device__ __forceinline__ float piece_sum(const float* cf, int w, int t, int n)
+{
+    return packed_at<T>(cf, w, 0, t, n) + (packed_at<T>(cf, w, 1, t, n) + packed_at<T>(cf, w, 2, t, n));
 }
 
 template <int CTRL>
@@ -201,33 +228,59 @@ __device__ __forceinline__ uint4 ld_words2(const uint64_t* base, int index)
         const_cast<uint64_t*>(base), 0, 0x7fffffff, 0x00020000);
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, index * 8, 0, 16 /* sc1 */));
 }
+// Start of a polling round: the loads after it must be issued again (nothing
+// in a polling loop writes memory, so without this the compiler may hoist
+// them out of the loop and spin on the first values).
+__device__ __forceinline__ void new_round()
+{
+    asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ uint64_t tag_f32(float v, uint32_t gen)
 {
     return (uint64_t)__float_as_uint(v) | ((uint64_t)gen << 32);
+}
+// Tag of a word handed over inside one XCD: the generation and the
+// producer's dispatch rotation (see the kernel).
+__device__ __forceinline__ uint32_t xcd_tag(uint32_t gen, uint32_t rot)
+{
+    return (gen << 3) | rot;
 }
 __device__ __forceinline__ void note_timeout(uint32_t* timeouts)
 {
     __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spins until the sentinel words of every lane that has them (index >= 0)
-// carry `gen` in their high 32 bits.  Returns false after a timeout (counted
-// once).
-__device__ __forceinline__ bool wait_sentinels(const uint64_t* base, int sent, const uint64_t* base2, int sent2,
-                                               uint32_t gen, long long t0, int lane, uint32_t* timeouts,
-                                               int site)
+// Reads the T consecutive words at base1 + idx1 and at base2 + idx2 (both
+// even) into v1 and v2, polling until every tag carries `gen`.  Each polling
+// round issues all its loads before it looks at any of them, so a round costs
+// one memory latency whatever T is.  Returns false after a timeout (counted
+// once; the values read so far are then meaningless).
+template <int T>
+__device__ __forceinline__ bool poll_words(const uint64_t* base1, int idx1, const uint64_t* base2, int idx2,
+                                           uint32_t gen, long long t0, int lane, float (&v1)[T], float (&v2)[T],
+                                           uint32_t* timeouts, int site)
 {
+    constexpr int NP = (T + 1) / 2;
     [[maybe_unused]] int rounds = 0;
     while (true) {
         ++rounds;
-        bool ok = true;
-        if (sent >= 0) {
-            const uint4 a = ld_words2(base, sent & ~1);
-            ok = ((sent & 1) ? a.w : a.y) == gen;
+        new_round();
+        uint4 a[NP], c[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            a[q] = ld_words2(base1, idx1 + 2 * q);
+            c[q] = ld_words2(base2, idx2 + 2 * q);
         }
-        if (sent2 >= 0) {
-            const uint4 a = ld_words2(base2, sent2 & ~1);
-            ok = ok && ((sent2 & 1) ? a.w : a.y) == gen;
+        bool ok = true;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            ok = ok && a[q].y == gen && c[q].y == gen && (2 * q + 1 >= T || (a[q].w == gen && c[q].w == gen));
+            v1[2 * q] = __uint_as_float(a[q].x);
+            v2[2 * q] = __uint_as_float(c[q].x);
+            if (2 * q + 1 < T) {
+                v1[2 * q + 1] = __uint_as_float(a[q].z);
+                v2[2 * q + 1] = __uint_as_float(c[q].z);
+            }
         }
         if (__all(ok)) {
             HC_COUNT(site, 0, rounds, lane == 0);
@@ -237,46 +290,6 @@ __device__ __forceinline__ bool wait_sentinels(const uint64_t* base, int sent, c
             if (lane == 0)
                 note_timeout(timeouts);
             return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
-// Reads the T consecutive words at base + idx (idx even) into v once their
-// tags carry `gen`, re-reading until they all do.  `live` false: nothing is
-// read (a timeout already happened).
-template <int T>
-__device__ __forceinline__ void read_words(const uint64_t* base, int idx, uint32_t gen, bool live, long long t0,
-                                           int lane, float (&v)[T], uint32_t* timeouts, int site)
-{
-    constexpr int NP = (T + 1) / 2;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        v[t] = 0.f;
-    bool done = !live;
-    [[maybe_unused]] int rounds = 0;
-    while (true) {
-        ++rounds;
-        if (!done) {
-            bool ok = true;
-#pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                const uint4 a = ld_words2(base, idx + 2 * q);
-                ok = ok && a.y == gen && (2 * q + 1 >= T || a.w == gen);
-                v[2 * q] = __uint_as_float(a.x);
-                if (2 * q + 1 < T)
-                    v[2 * q + 1] = __uint_as_float(a.z);
-            }
-            done = ok;
-        }
-        if (__all(done)) {
-            HC_COUNT(site, 1, rounds, lane == 0);
-            return;
-        }
-        if (wall_clock64() - t0 > kWaitTicks) {
-            if (lane == 0)
-                note_timeout(timeouts);
-            return;
         }
         __builtin_amdgcn_s_sleep(1);
     }
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     s.gen = reinterpret_cast<uint32_t*>(s.lo + kLoWords);
     s.timeouts = s.gen + kDecWGs;
     const int b = blockIdx.x;
-    const int x = b & 7;   // XCD
+    const int x = b & 7;   // group (all its workgroups share one XCD)
     const int i = b >> 3;  // index inside the XCD, 0..31
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -357,8 +370,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // seen.  Every lane loads the counter (no per-lane branch); the value is
     // used only after the weights have landed.
     uint32_t seen = __hip_atomic_load(&s.gen[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0 && __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) != x)
-        note_timeout(s.timeouts);  // not on the XCD the hand-offs assume: results invalid
+    // The dispatcher deals workgroups to the XCDs round robin, starting where
+    // the previous dispatch stopped: workgroup b runs on XCD (b + r) % 8 with
+    // one rotation r for the whole launch, so the workgroups of one group x
+    // share an L2 whatever r is.  Each workgroup puts its own r into the tags
+    // of the words it hands over inside its XCD, and a reducer accepts only
+    // its own r: a producer that ran on another XCD shows up as an expired
+    // (counted) wait, never as a silent stale read.
+    const uint32_t rot = (__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) - (uint32_t)x) & 7u;
     HC_PROBE(0, threadIdx.x == 0);
     // Loads issued before the first wait are unconditional (items past the end
     // re-read item 0; a missing pending re-reads R): a conditional load makes
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         const int d = i;
         uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kTileChunks);     // [3][T][kYRow]
         float* const sspart = reinterpret_cast<float*>(ypl + 3 * T * kYRow);       // [T][160]
-        f32x4_t* const comb = reinterpret_cast<f32x4_t*>(sspart + T * kStageItems);  // [3][64]
+        f32x4_t* const comb = reinterpret_cast<f32x4_t*>(sspart + T * kStageItems);  // [6][chains][64]
 
         // (1) the W_down tile: rows 40 x + row, columns 640 d + 8 j ..
         for (int q = wave; q < kTileInstr; q += 8) {
@@ -417,57 +436,45 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         wait_all_loads();  // this wave's part of the tile is in LDS
         wg_barrier();      // B1: activations staged, W_down tile complete
         HC_PROBE(1, threadIdx.x == 0);
+        pin(seen);
+        const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
 
         // (3) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
         //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over
-        //     K steps 10 (w / 3) .. +9 of 32 columns
-        f32x4_t dacc = {0.f, 0.f, 0.f, 0.f};
+        //     K steps 10 (w / 3) .. +9 of 32 columns.  A rows are (piece,
+        //     token) pairs in the planes' own order (row p T + t: piece p of
+        //     token t), so one chain of MFMAs carries all three pieces when
+        //     3 T <= 16, two chains (pieces 0-1, then piece 2) otherwise.
         if (wave < 6) {
             const int nb = wave % 3, kh = wave / 3;
             const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
-            // all operands first (one LDS latency, not ten); A rows >= T
-            // repeat token T - 1: they only feed D rows >= T, never stored
-            const int mc = m < T ? m : T - 1;
-            uint4 wb[10], ah[10], am[10], al[10];
+            // all operands first (one LDS latency, not ten); A rows past the
+            // pieces re-read row 0: they only feed D rows nobody reads
+            const int r0 = m < kPackRows<T> ? m : 0;
+            const int r1 = 2 * T + (m < T ? m : 0);
+            uint4 wb[10], a0[10], a1[10];
 #pragma unroll
             for (int qq = 0; qq < 10; ++qq) {
                 const int q = 10 * kh + qq;
                 const int col = 32 * q + 8 * g;
                 wb[qq] = tile[tile_pos<kDnRowChunks>(row, 4 * q + g)];
-                ah[qq] = *reinterpret_cast<const uint4*>(&ypl[(0 * T + mc) * kYRow + col]);
-                am[qq] = *reinterpret_cast<const uint4*>(&ypl[(1 * T + mc) * kYRow + col]);
-                al[qq] = *reinterpret_cast<const uint4*>(&ypl[(2 * T + mc) * kYRow + col]);
+                a0[qq] = *reinterpret_cast<const uint4*>(&ypl[r0 * kYRow + col]);
+                if (kChains<T> == 2)
+                    a1[qq] = *reinterpret_cast<const uint4*>(&ypl[r1 * kYRow + col]);
             }
-            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
             for (int qq = 0; qq < 10; ++qq) {
-                a0 = mfma16(ah[qq], wb[qq], a0);
-                a1 = mfma16(am[qq], wb[qq], a1);
-                a2 = mfma16(al[qq], wb[qq], a2);
+                acc0 = mfma16(a0[qq], wb[qq], acc0);
+                if (kChains<T> == 2)
+                    acc1 = mfma16(a1[qq], wb[qq], acc1);
             }
-            dacc = a0 + (a1 + a2);
-            if (kh == 1)
-                comb[nb * 64 + lane] = dacc;
-        }
-        HC_PROBE(2, threadIdx.x == 0);
-        wg_barrier();  // Bc1: second K halves in LDS
-        pin(seen);
-        const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
-
-        if (wave < 3) {
-            // (4) partial dots of rows 16 nb + n, tokens 4 g + e, into the XCD's L2
-            //     (all 8 token slots, whole lines; slots >= T hold values nobody reads)
-            dacc = dacc + comb[wave * 64 + lane];
-            const int row = 16 * wave + n;
-            if (row < kDecRowsPerXcd && g < 2) {
-                uint64_t* dst = s.part + (((size_t)x * kDecDownPerXcd + d) * kDecRowsPerXcd + row) * kDecMaxT + 4 * g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    st_word_xcd(dst + e, tag_f32(dacc[e], gen));
-            }
-        } else if (wave == 3) {
-            // (4') the slice's sum of squares per token: lane 8 t + p sums 20
-            //      of token t's 160 item sums, then the 8 lanes combine theirs
+            comb[(wave * kChains<T>) * 64 + lane] = acc0;
+            if (kChains<T> == 2)
+                comb[(wave * kChains<T> + 1) * 64 + lane] = acc1;
+        } else if (wave == 6) {
+            // (3') meanwhile, the slice's sum of squares per token: lane 8 t + p
+            //      sums 20 of token t's 160 item sums, then the 8 lanes combine theirs
             const int tt = lane >> 3, p = lane & 7;
             float ss = 0.f;
             if (tt < T) {
@@ -477,7 +484,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             ss = sum8(ss);
             if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
-                st_word_xcd(&s.ssq[((size_t)x * kDecDownPerXcd + d) * kSsqLine + 8 * p + tt], tag_f32(p == 0 ? ss : 0.f, gen));
+                st_word_xcd(&s.ssq[((size_t)x * kDecDownPerXcd + d) * kSsqLine + 8 * p + tt],
+                            tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
+        }
+        HC_PROBE(2, threadIdx.x == 0);
+        wg_barrier();  // Bc1: every product block in LDS
+
+        if (wave < 6) {
+            // (4) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g,
+            //     into the XCD's L2: per K half hi + (mid + lo3), then the two
+            //     halves (all 8 token slots, whole lines; slots >= T hold 0)
+            const float* cf = reinterpret_cast<const float*>(comb);
+            const int nb = wave % 3, t = 4 * (wave / 3) + g;
+            const int row = 16 * nb + n;
+            if (row < kDecRowsPerXcd) {
+                const float v = t < T ? piece_sum<T>(cf, nb, t, n) + piece_sum<T>(cf, nb + 3, t, n) : 0.f;
+                st_word_xcd(s.part + (((size_t)x * kDecDownPerXcd + d) * kDecRowsPerXcd + row) * kDecMaxT + t,
+                            tag_f32(v, xcd_tag(gen, rot)));
+            }
         }
         HC_PROBE(3, threadIdx.x == 0);
         if (threadIdx.x == 0)
@@ -490,27 +514,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int c0 = kDecUpCols * (kDecUpPerXcd * x + u);  // first output column
     uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kTileChunks);  // [3][T][kLoRow]
     float* const rpl = reinterpret_cast<float*>(lpl + 3 * T * kLoRow);      // [T][80]: R' of tile row 20 s + r
+    f32x4_t* const ucomb = reinterpret_cast<f32x4_t*>(rpl + T * kUpRows);   // [5 waves][chains][64]
 
-    // (0) a reducer first touches (plain loads, which keep the lines in this
-    //     XCD's L2) the lines it will poll: the 16 producers' partial rows
-    //     3 u .. 3 u + 2 and their sums of squares.  Polls then hit L2 and see
-    //     a producer's store as soon as it lands, instead of each round
-    //     fetching the line from memory.  (Only lines written inside this XCD
-    //     are touched this way.)
-    if (wave == 0 && u < kDecReducers) {
-        const int src = lane & 15, k = lane >> 4;  // k 0..2: partial lines, 3: sums of squares
-        const int rowl = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
-        const uint64_t* line = k < 3 ? s.part + (((size_t)x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowl) * kDecMaxT
-                                     : s.ssq + ((size_t)x * kDecDownPerXcd + src) * kSsqLine;
-        const uint32_t touched = *reinterpret_cast<const volatile uint32_t*>(line);
-        asm volatile("" ::"v"(touched));
-    }
     // (1) the W_up tile: rows s * 2560 + c0 + r (tile row 20 s + r)
     for (int q = wave; q < kTileInstr; q += 8) {
         int row, j;
         tile_lane<kUpRowChunks>(q, lane, row, j);
         const int k = (row / kDecUpCols) * kWidth + c0 + row % kDecUpCols;
         dma16(W_up + (size_t)k * kRank + 8 * j, tile + 64 * q);
+    }
+    // (2) a reducer touches (plain loads, which keep the lines in this XCD's
+    //     L2) the lines it will poll: the 16 producers' partial rows
+    //     3 u .. 3 u + 2 and their sums of squares.  Polls then hit L2 and see
+    //     a producer's store as soon as it lands, instead of each round
+    //     fetching the line from memory.  (Only lines written inside this XCD
+    //     are touched this way.)  The loaded value is consumed only after the
+    //     weights have landed, so nothing waits for it before then.
+    uint32_t touched = 0;
+    if (wave == 0 && u < kDecReducers) {
+        const int src = lane & 15, k = lane >> 4;  // k 0..2: partial lines, 3: sums of squares
+        const int rowl = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
+        const uint64_t* line = k < 3 ? s.part + (((size_t)x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowl) * kDecMaxT
+                                     : s.ssq + ((size_t)x * kDecDownPerXcd + src) * kSsqLine;
+        touched = *reinterpret_cast<const uint32_t*>(line);  // (not volatile: that would wait here)
     }
     // R and pending of the same 80 (stream, column) pairs, for the mix
     float mr[2], mp[2];
@@ -530,6 +556,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             rpl[it] = P ? mr[pass] + mp[pass] : mr[pass];  // it = 80 t + row
     }
     wait_all_loads();  // every load of this CU has landed: from here on, hand-off loads run at cache latency
+    asm volatile("" ::"v"(touched));
     wg_barrier();      // B1
     HC_PROBE(1, threadIdx.x == 0);
     pin(seen);
@@ -547,11 +574,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const int pidx = ((x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowc) * kDecMaxT;
             const int sidx = (x * kDecDownPerXcd + src) * kSsqLine;
             const long long t0 = wall_clock64();
-            const bool live = wait_sentinels(s.part, valid ? pidx + T - 1 : -1, s.ssq, sidx + T - 1, gen, t0, lane,
-                                             s.timeouts, 0);
             float v[T], q[T];
-            read_words<T>(s.part, pidx, gen, live, t0, lane, v, s.timeouts, 0);
-            read_words<T>(s.ssq, sidx, gen, live, t0, lane, q, s.timeouts, 1);
+            poll_words<T>(s.part, pidx, s.ssq, sidx, xcd_tag(gen, rot), t0, lane, v, q, s.timeouts, 0);
             HC_PROBE(12, lane == 0);
             float mine = 0.f;  // lo of row 3 u + r, token `src`
 #pragma unroll
@@ -574,48 +598,37 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     st_word(&s.lo[lo_word(y, x, u, src, r)], word);
             HC_PROBE(13, lane == 0);
         }
-        // (6) hop 2, first: wait for this XCD's reducers (the last row of
-        //     each, last token).  The other XCDs run in step with this one, so
-        //     their lo is then due too; polling only local words keeps the
-        //     device-wide traffic to one read per workgroup.
-        const long long t0 = wall_clock64();
-        const int sent = lane < kDecReducers ? lo_word(x, x, lane, T - 1, 2) : -1;
-        HC_PROBE(15, lane == 0);
-        wait_sentinels(s.lo, sent, s.lo, -1, gen, t0, lane, s.timeouts, 2);  // (a timeout is counted; the reads below are bounded too)
-        HC_PROBE(14, lane == 0);
     }
     wg_barrier();  // Bs
-    if (wave < 4) {
-        // (6) hop 2, then: wave w reads the reducers of XCDs 2 w and 2 w + 1
-        //     (slot = reducer, token, pair of rows), re-reading words whose
-        //     tag is still old, and stages the 3 bf16 pieces of each value
-        constexpr int NS = (2 * kDecReducers * T * 2 + 63) / 64;  // slots per lane
+    {
+        // (6) hop 2: wave w polls the lo words of XCD w's reducers (slot =
+        //     reducer, token, pair of rows) until every tag is current, then
+        //     stages the 3 bf16 pieces of each value.  (Waves start after this
+        //     workgroup's own reducer is done, so their cold loads do not
+        //     queue in front of its L2 polls.)
+        constexpr int NSL = kDecReducers * T * 2;  // slots per wave
+        constexpr int NS = (NSL + 63) / 64;        // slots per lane
         const long long t0 = wall_clock64();
         uint4 lw[NS];
-        bool done[NS];
         int widx[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-            const int sl = lane + 64 * k;
+            const int sl = lane + 64 * k < NSL ? lane + 64 * k : 0;  // (past the end: re-read slot 0)
             const int pair = sl & 1, rest = sl >> 1;
-            const int tt = rest % T, red = rest / T;  // red: 0 .. 27
-            const int xs = 2 * wave + red / kDecReducers, us = red % kDecReducers;
-            widx[k] = lo_word(x, xs, us, tt, 2 * pair);
-            lw[k] = make_uint4(0, 0, 0, 0);
-            done[k] = sl >= 2 * kDecReducers * T * 2;
+            const int tt = rest % T, us = rest / T;  // us: reducer 0 .. 13
+            widx[k] = lo_word(x, wave, us, tt, 2 * pair);
         }
         [[maybe_unused]] int rounds = 0;
         while (true) {
             ++rounds;
+            new_round();
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                lw[k] = ld_words2(s.lo, widx[k]);
             bool all = true;
 #pragma unroll
-            for (int k = 0; k < NS; ++k) {
-                if (!done[k]) {
-                    lw[k] = ld_words2(s.lo, widx[k]);
-                    done[k] = lw[k].y == gen && lw[k].w == gen;
-                }
-                all = all && done[k];
-            }
+            for (int k = 0; k < NS; ++k)
+                all = all && lw[k].y == gen && lw[k].w == gen;
             if (__all(all)) {
                 HC_COUNT(2, 1, rounds, wave == 0 && lane == 0);
                 break;
@@ -627,19 +640,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             __builtin_amdgcn_s_sleep(2);
         }
+        HC_PROBE(14, wave == 0 && lane == 0);
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             const int sl = lane + 64 * k;
-            if (sl < 2 * kDecReducers * T * 2) {
+            if (sl < NSL) {
                 const int pair = sl & 1, rest = sl >> 1;
-                const int tt = rest % T, red = rest / T;
-                const int xs = 2 * wave + red / kDecReducers, us = red % kDecReducers;
+                const int tt = rest % T, us = rest / T;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int rr = 2 * pair + h;               // row of the reducer, 0..3
                     const int rowl = kDecRedRows * us + rr;    // row of the XCD, 0..39
                     if (rr < kDecRedRows && rowl < kDecRowsPerXcd) {
-                        const int jr = kDecRowsPerXcd * xs + rowl;
+                        const int jr = kDecRowsPerXcd * wave + rowl;
                         uint32_t hb, mb, lb;
                         split3(__uint_as_float(h ? lw[k].z : lw[k].x), hb, mb, lb);
                         lpl[(0 * T + tt) * kLoRow + jr] = (uint16_t)hb;
@@ -656,34 +669,43 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
     if (wave < kDecUpCols / 4) {
         // (7) up projection: wave w < 5 takes output columns c0 + 4 w .. +3
-        //     (slot n = 4 column + stream), all 10 K steps; gated = up
-        //     (identity epilogue); then the mix of the 4 streams of a column
+        //     (slot n = 4 column + stream), all 10 K steps, A rows packed as
+        //     in the down projection; gated = up (identity epilogue); then the
+        //     mix of the 4 streams of a column
         const int cc = n >> 2, st = n & 3;
         const int row = st * kDecUpCols + 4 * wave + cc;
-        const int mc = m < T ? m : T - 1;  // (rows >= T feed only D rows >= T)
-        uint4 wb[10], ah[10], am[10], al[10];
+        const int r0 = m < kPackRows<T> ? m : 0;
+        const int r1 = 2 * T + (m < T ? m : 0);
+        uint4 wb[10], a0[10], a1[10];
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             const int jc = 32 * q + 8 * g;
             wb[q] = tile[tile_pos<kUpRowChunks>(row, 4 * q + g)];
-            ah[q] = *reinterpret_cast<const uint4*>(&lpl[(0 * T + mc) * kLoRow + jc]);
-            am[q] = *reinterpret_cast<const uint4*>(&lpl[(1 * T + mc) * kLoRow + jc]);
-            al[q] = *reinterpret_cast<const uint4*>(&lpl[(2 * T + mc) * kLoRow + jc]);
+            a0[q] = *reinterpret_cast<const uint4*>(&lpl[r0 * kLoRow + jc]);
+            if (kChains<T> == 2)
+                a1[q] = *reinterpret_cast<const uint4*>(&lpl[r1 * kLoRow + jc]);
         }
-        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
-            a0 = mfma16(ah[q], wb[q], a0);
-            a1 = mfma16(am[q], wb[q], a1);
-            a2 = mfma16(al[q], wb[q], a2);
+            acc0 = mfma16(a0[q], wb[q], acc0);
+            if (kChains<T> == 2)
+                acc1 = mfma16(a1[q], wb[q], acc1);
         }
-        const f32x4_t uacc = a0 + (a1 + a2);
+        // a token's pieces sit in other lanes: through this wave's own LDS block
+        f32x4_t* const ub = ucomb + wave * kChains<T> * 64;
+        ub[lane] = acc0;
+        if (kChains<T> == 2)
+            ub[64 + lane] = acc1;
+        asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
+        const float* cf = reinterpret_cast<const float*>(ub);
         const int c = c0 + 4 * wave + cc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tt = 4 * g + e;
+            const float up = tt < T ? piece_sum<T>(cf, 0, tt, n) : 0.f;
             const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
-            const float mixed = sum4(uacc[e] * rp);  // (s0 + s1) + (s2 + s3)
+            const float mixed = sum4(up * rp);  // (s0 + s1) + (s2 + s3)
             if (st == 0 && tt < T) {
                 const size_t o = (size_t)tt * kWidth + c;
                 out_mixed[o] = mixed;

@@ -15,8 +15,9 @@ constexpr float kEps = 1e-6f;
 
 // ---------------------------------------------------------------------------
 // Short-window path (T <= kDecMaxT): one launch of kDecWGs workgroups, one
-// per CU, each of 8 waves.  Workgroup b runs on XCD x = b % 8 (the dispatcher
-// deals workgroups to the 8 XCDs round robin; the kernel checks it); i = b / 8.
+// per CU, each of 8 waves.  Workgroup b belongs to group x = b % 8, i = b / 8;
+// the dispatcher deals workgroups to the 8 XCDs round robin, so the 32
+// workgroups of a group share one XCD and its L2 (the kernel checks it).
 // Each XCD's 32 workgroups split into two roles, so that no CU polls while
 // its own weight loads are in flight:
 //   down (i < 16, d = i): W_down rows [40 x, 40 x + 40) x columns
@@ -48,7 +49,7 @@ struct DecodeScratch {
     uint64_t* ssq;       // [8 xcd][16 down wg][kDecMaxT]: column-slice sums of squares (XCD-local)
     uint64_t* lo;        // [kDecMaxT][kRank]: lo (device-wide)
     uint32_t* gen;       // [kDecWGs]: launches completed by each workgroup
-    uint32_t* timeouts;  // [1]: expired bounded waits and misplaced workgroups
+    uint32_t* timeouts;  // [1]: expired bounded waits (a workgroup off its group's XCD expires one)
 };
 
 size_t decode_scratch_bytes();

@@ -21,7 +21,16 @@ def gpu():
     from hyper_connection_residual_amd import binding
     binding.library()
     yield
-    assert binding.hc_timeouts() == 0, "a bounded wait expired during the GPU tests"
+
+
+@pytest.fixture(autouse=True)
+def no_expired_waits():
+    """Every test leaves the default stream's bounded-wait counter at zero."""
+    from hyper_connection_residual_amd import binding
+    binding.hc_timeouts()  # (reading clears it)
+    yield
+    n = binding.hc_timeouts()
+    assert n == 0, "%d bounded waits expired (or workgroups ran off their XCD) during this test" % n
 
 
 def _case(label):
@@ -212,3 +221,59 @@ def test_two_streams_have_separate_scratch():
         with torch.cuda.stream(s2):
             gb = hip_read(db, stream=s2)[0]
         assert np.array_equal(ga, ref_a) and np.array_equal(gb, ref_b)
+
+
+def test_graph_replay_matches_eager():
+    """Reads captured in a HIP graph (short windows with pending, and one wide
+    read) replay to the same bits as eager reads, replay after replay, with
+    eager reads on the same stream and synchronisations in between."""
+    import torch
+    from hyper_connection_residual_amd import binding
+    _case("graph replay: T=1, 5, 8 with pending and T=40 without, 4 replays")
+    inps = [wl.config_inputs(2, T=T, weight_set=30 + T) for T in (1, 5, 8)] + [wl.config_inputs(1, T=40)]
+    devs = [to_device(i) for i in inps]
+    log = []
+
+    def expired(label, s=None):
+        torch.cuda.synchronize()
+        log.append((label, binding.hc_timeouts(None), binding.hc_timeouts(s) if s is not None else 0))
+
+    expired("before")
+    refs = [hip_read(d) for d in devs]
+    expired("eager references")
+    gs = torch.cuda.Stream()
+    outs = [(torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.float32, device="cuda"),
+             torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.int16, device="cuda"),
+             torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.int16, device="cuda")) for d in devs]
+
+    def issue():
+        for d, o in zip(devs, outs):
+            st = binding.hc_read(d["R"].shape[0], d["R"], d["pending"], d["w_norm"], d["W_down"], d["W_up"],
+                                 o[0], o[1], o[2], gs)
+            assert st == 0, binding.hc_status_string(st)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gs):
+        issue()  # eager first calls on this stream allocate its scratch (not allowed under capture)
+    expired("eager on the capture stream", gs)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        issue()
+    expired("capture", gs)
+    other = to_device(wl.config_inputs(2, T=6, weight_set=44))
+    for rep in range(4):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(gs):
+            g.replay()
+        expired("replay %d" % rep, gs)
+        hip_read(other, stream=gs)  # eager work on the same stream between replays
+        expired("eager after replay %d" % rep, gs)
+        for k, (o, ref) in enumerate(zip(outs, refs)):
+            got = (o[0].cpu().numpy(), o[1].cpu().numpy().view(np.uint16), o[2].cpu().numpy().view(np.uint16))
+            for a, b in zip(got, ref):
+                assert np.array_equal(a, b), "replay %d, read %d differs from the eager read" % (rep, k)
+    print("expired waits (default stream, capture stream) by phase: %s" % log, flush=True)
+    assert all(a == 0 and b == 0 for _, a, b in log), "expired waits: %s" % log
