@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (the reference for "
                          "scaling the HBM byte counters of a profiler run)")
-    ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_prefill8192_hbm_bytes.md"),
+    ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_wide_reads_hbm_bytes.md"),
                     help="summary of the profiler's FETCH_SIZE / WRITE_SIZE runs; its figure is "
                          "reported only if it was measured on the current kernel source")
     return ap.parse_args()

@@ -1,10 +1,12 @@
 """Summaries of rocprofv3 CSV output for the read's kernels (markdown).
 
     python -m hyper_connection_residual_amd.rocprof_summary stats <kernel_stats.csv> > out.md
+    python -m hyper_connection_residual_amd.rocprof_summary trace <kernel_trace.csv> > out.md
     python -m hyper_connection_residual_amd.rocprof_summary bytes <fetch counter_collection.csv> \
         <write counter_collection.csv> > out.md
 
-`stats` tabulates per-kernel durations.  `bytes` tabulates HBM bytes per
+`stats` tabulates per-kernel durations; `trace` does the same per (kernel,
+workgroup count), which separates launches of one kernel at different sizes.  `bytes` tabulates HBM bytes per
 dispatch from one FETCH_SIZE run and one WRITE_SIZE run (KiB per dispatch).
 Both counters are scaled by what they read for a plain device-to-device copy of
 known size run in the same process (the runtime's copy kernel, which bench.py
@@ -45,6 +47,21 @@ def stats(path: str) -> str:
                 short_name(row["Name"]), row["Calls"], float(row["AverageNs"]) / 1e3,
                 float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3,
                 float(row["TotalDurationNs"]) / 1e6))
+    return "\n".join(out)
+
+
+def trace(path: str) -> str:
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            wgs = int(row["Grid_Size_X"]) // max(1, int(row["Workgroup_Size_X"]))
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            groups[(short_name(row["Kernel_Name"]), wgs)].append(dur)
+    out = ["| kernel | workgroups | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    for (name, wgs), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = sorted(d)
+        out.append("| %s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
+            name, wgs, len(d), sum(d) / len(d), d[len(d) // 2], d[0], d[-1]))
     return "\n".join(out)
 
 
@@ -98,6 +115,8 @@ def read_traffic(md_path: str):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
+    elif sys.argv[1] == "trace":
+        print(trace(sys.argv[2]))
     elif sys.argv[1] == "bytes":
         print(traffic(sys.argv[2], sys.argv[3]))
     else:
