@@ -564,38 +564,107 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
     if (wave == 0) {
         if (u < kDecReducers) {
-            // (5) hop 1: rows 3 u + r (r = lane / 16 < 3) over the XCD's 16
-            //     partials (lane % 16 = down workgroup), each stream's rs from
-            //     its 4 slices' sums of squares; lo published device-wide
-            const int r = lane >> 4, src = lane & 15;
-            const int row = kDecRedRows * u + r;
-            const bool valid = r < kDecRedRows && row < kDecRowsPerXcd;
-            const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
-            const int pidx = ((x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowc) * kDecMaxT;
-            const int sidx = (x * kDecDownPerXcd + src) * kSsqLine;
-            const long long t0 = wall_clock64();
-            float v[T], q[T];
-            poll_words<T>(s.part, pidx, s.ssq, sidx, xcd_tag(gen, rot), t0, lane, v, q, s.timeouts, 0);
-            HC_PROBE(12, lane == 0);
-            float mine = 0.f;  // lo of row 3 u + r, token `src`
+            // (5) hop 1: lo rows 3 u .. 3 u + 2 of this XCD from its 16
+            //     down workgroups' partials, each stream's rs from its 4
+            //     slices' sums of squares; lo published device-wide.  Up to 4
+            //     tokens, a lane group per row (rows in parallel, tokens in
+            //     turn); from 5 tokens, a lane group per pair of tokens (one
+            //     load per row per polling round, rows in turn).
+            if constexpr (T <= 4) {
+                // lane = src + 16 r: row 3 u + r (r < 3) of down workgroup src
+                const int r = lane >> 4, src = lane & 15;
+                const int row = kDecRedRows * u + r;
+                const bool valid = r < kDecRedRows && row < kDecRowsPerXcd;
+                const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
+                const int pidx = ((x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowc) * kDecMaxT;
+                const int sidx = (x * kDecDownPerXcd + src) * kSsqLine;
+                const long long t0 = wall_clock64();
+                float v[T], q[T];
+                poll_words<T>(s.part, pidx, s.ssq, sidx, xcd_tag(gen, rot), t0, lane, v, q, s.timeouts, 0);
+                HC_PROBE(12, lane == 0);
+                float mine = 0.f;  // lo of row 3 u + r, token `src`
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
-                const float ss = sum4(q[t]);
-                const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
-                const float y = sum4(v[t]) * rs;
-                const float y01 = y + dpp<0x141>(y);      // row_half_mirror: (s0 + s1), (s2 + s3)
-                const float lo = y01 + dpp<0x140>(y01);   // row_mirror: (s0 + s1) + (s2 + s3)
-                if (src == t)
-                    mine = lo;
+                for (int t = 0; t < T; ++t) {
+                    // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
+                    const float ss = sum4(q[t]);
+                    const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+                    const float y = sum4(v[t]) * rs;
+                    const float y01 = y + dpp<0x141>(y);      // row_half_mirror: (s0 + s1), (s2 + s3)
+                    const float lo = y01 + dpp<0x140>(y01);   // row_mirror: (s0 + s1) + (s2 + s3)
+                    if (src == t)
+                        mine = lo;
+                }
+                // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
+                // this reducer, 0 in the padding
+                const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
+#pragma unroll
+                for (int y = 0; y < kDecXcds; ++y)
+                    if (src < kDecMaxT)
+                        st_word(&s.lo[lo_word(y, x, u, src, r)], word);
+            } else {
+                // lane = src + 16 q: tokens 2 q, 2 q + 1 of down workgroup src
+                // (a polling round is 3 row loads and 1 sum-of-squares load)
+                const int src = lane & 15, q = lane >> 4;
+                const int pbase = (x * kDecDownPerXcd + src) * kDecRowsPerXcd;
+                int pidx[kDecRedRows];
+#pragma unroll
+                for (int rr = 0; rr < kDecRedRows; ++rr) {
+                    const int row = kDecRedRows * u + rr;
+                    pidx[rr] = (pbase + (row < kDecRowsPerXcd ? row : kDecRowsPerXcd - 1)) * kDecMaxT + 2 * q;
+                }
+                const int sidx = (x * kDecDownPerXcd + src) * kSsqLine + 2 * q;
+                const uint32_t htag = xcd_tag(gen, rot);
+                const long long t0 = wall_clock64();
+                uint4 pw[kDecRedRows], sw;
+                [[maybe_unused]] int rounds = 0;
+                while (true) {
+                    ++rounds;
+                    new_round();
+#pragma unroll
+                    for (int rr = 0; rr < kDecRedRows; ++rr)
+                        pw[rr] = ld_words2(s.part, pidx[rr]);
+                    sw = ld_words2(s.ssq, sidx);
+                    bool ok = sw.y == htag && sw.w == htag;
+#pragma unroll
+                    for (int rr = 0; rr < kDecRedRows; ++rr)
+                        ok = ok && pw[rr].y == htag && pw[rr].w == htag;
+                    if (__all(ok)) {
+                        HC_COUNT(0, 0, rounds, lane == 0);
+                        break;
+                    }
+                    if (wall_clock64() - t0 > kWaitTicks) {
+                        if (lane == 0)
+                            note_timeout(s.timeouts);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                HC_PROBE(12, lane == 0);
+                float lo[kDecRedRows][2];  // [row][token 2 q + h], the same in all 16 lanes of q
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
+                    const float ss = sum4(__uint_as_float(h ? sw.z : sw.x));
+                    const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+#pragma unroll
+                    for (int rr = 0; rr < kDecRedRows; ++rr) {
+                        const float y = sum4(__uint_as_float(h ? pw[rr].z : pw[rr].x)) * rs;
+                        const float y01 = y + dpp<0x141>(y);     // row_half_mirror: (s0 + s1), (s2 + s3)
+                        lo[rr][h] = y01 + dpp<0x140>(y01);       // row_mirror: (s0 + s1) + (s2 + s3)
+                    }
+                }
+                // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
+                // this reducer, 0 in the padding; lane src < 8 of q writes row
+                // src / 2, token 2 q + src % 2
+                const int rr = src >> 1, h = src & 1, tok = 2 * q + h;
+                const float mine = rr == 0 ? lo[0][h] : rr == 1 ? lo[1][h] : lo[2][h];
+                const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
+                const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
+#pragma unroll
+                for (int y = 0; y < kDecXcds; ++y)
+                    if (src < 8)
+                        st_word(&s.lo[lo_word(y, x, u, tok, rr)], word);
             }
-            // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
-            // this reducer, 0 in the padding
-            const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
-#pragma unroll
-            for (int y = 0; y < kDecXcds; ++y)
-                if (src < kDecMaxT)
-                    st_word(&s.lo[lo_word(y, x, u, src, r)], word);
             HC_PROBE(13, lane == 0);
         }
     }
