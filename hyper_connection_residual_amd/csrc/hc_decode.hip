@@ -224,13 +224,16 @@ __device__ __forceinline__ void st_word_xcd(uint64_t* p, uint64_t v)
 // stale line.
 __device__ __forceinline__ uint4 ld_words2(const uint64_t* base, int index)
 {
+    // An opaque copy of the (wave-uniform, scalar) base: the compiler can
+    // neither merge two polling loads nor move one out of its loop (it does
+    // not treat a memory clobber as reaching buffer loads).
+    asm volatile("" : "+s"(base));
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint64_t*>(base), 0, 0x7fffffff, 0x00020000);
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, index * 8, 0, 16 /* sc1 */));
 }
-// Start of a polling round: the loads after it must be issued again (nothing
-// in a polling loop writes memory, so without this the compiler may hoist
-// them out of the loop and spin on the first values).
+// Start of a polling round (a compiler barrier; each polling load's opaque
+// base is what keeps the loads inside their loop).
 __device__ __forceinline__ void new_round()
 {
     asm volatile("" ::: "memory");
