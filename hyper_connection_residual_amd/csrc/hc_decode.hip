@@ -14,16 +14,18 @@
 // gfx950 design (the pages' kernels were written for RDNA2, Turing, Ada and
 // Arc; none of their mechanics is reused):
 //
-// * 256 workgroups x 8 waves, one per CU, each streaming 51 KB of weights.  A
-//   CU serves its vector memory requests in order across its waves (measured:
-//   a load that hits L2 in 0.08 us takes over 1 us while another wave of the
-//   CU has cold loads outstanding), so a CU that polls for a hand-off while
-//   its own weight loads are in flight waits for all of them.  The workgroups
-//   of each XCD therefore split in two roles that never overlap: 16 "down"
-//   workgroups stream W_down, publish partial dots and end without waiting for
-//   anything; 16 "up" workgroups stream W_up and do every wait after it has
-//   landed.  Both halves issue all their loads at entry, so the whole 13 MB is
-//   in flight at once.
+// * 256 workgroups x 8 waves, one per CU.  Each workgroup streams a 25.6 KB
+//   tile of W_down (40 rows x 320 columns) at entry and a 25.6 KB tile of
+//   W_up (10 output columns x 4 streams) later.  A CU serves its vector
+//   memory requests in order across its waves (measured: a load that hits L2
+//   in 0.08 us takes over 1 us while another wave of the CU has cold loads
+//   outstanding), so a poll issued behind a tile waits for the whole tile.
+//   Most workgroups issue their W_up tile as soon as their partial dots are
+//   stored; the 14 per XCD that reduce partials (below) issue it after that
+//   reduction, so their polls never queue behind it.  (Measured: issuing the
+//   W_up tiles at entry makes the W_down tiles land 1 us later, since the
+//   memory system shares its bandwidth between everything in flight; issuing
+//   them before the reduction delays the reduction.  Both are slower.)
 // * The tiles go straight from memory into LDS (global_load_lds_dwordx4), each
 //   wave instruction fetching 8 whole 128-byte lines.  Measured on MI355X:
 //   loading the same bytes in the matrix cores' operand layout (16 rows x 64
@@ -34,11 +36,12 @@
 // * Both projections run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
 //   with tokens as the M dimension.  Each fp32 activation is split exactly into
 //   three bf16 pieces (hi + mid + lo3 == x), so every product is exact and the
-//   result stays fp32-faithful.  Each piece has its own accumulator (three
-//   independent MFMA chains).
-// * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): up
-//   workgroups reduce the 16 partials of 3 rows each through the XCD's L2
-//   (hop 1) and publish lo device-wide; every up workgroup gathers all of lo
+//   result stays fp32-faithful.  The pieces of all tokens share the MFMA's
+//   rows (row p T + t: piece p of token t), so one chain of MFMAs carries them
+//   when 3 T <= 16, two chains otherwise.
+// * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): 14
+//   of its 32 workgroups each reduce the 32 partials of 3 rows through the
+//   XCD's L2 (hop 1) and publish lo device-wide; every workgroup gathers all of lo
 //   (hop 2).  Hand-off words are 64 bits holding the payload and the launch's
 //   generation number, written once with one store; a consumer polls the data
 //   words themselves (device-coherent loads, which see a write-through store
@@ -72,32 +75,30 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr long long kWaitTicks = 5000000;  // 50 ms of the 100 MHz wall clock
-constexpr int kTileChunks = 3200;           // 16-byte chunks in either weight tile (51,200 bytes)
-constexpr int kTileInstr = kTileChunks / 64;  // wave instructions per tile (50)
-constexpr int kDnRowChunks = kDecDownCols / 8;  // chunks per W_down tile row (80)
-constexpr int kUpRowChunks = kRank / 8;         // chunks per W_up tile row (40)
-constexpr int kUpRows = 4 * kDecUpCols;         // W_up tile rows (80): row 20 s + r
-constexpr int kStageItems = kDecDownCols / 4;   // float4 activation items per token (160)
-constexpr int kYRow = kDecDownCols + 8;         // padded LDS row of an activation plane (bf16)
-constexpr int kLoRow = kRank + 8;               // padded LDS row of a lo plane (bf16)
+constexpr int kTileChunks = 1600;           // 16-byte chunks in either weight tile (25,600 bytes)
+constexpr int kTileInstr = kTileChunks / 64;  // wave instructions per tile (25)
+constexpr int kRowChunks = kRank / 8;       // chunks per row of either tile (40: 320 bf16)
+constexpr int kUpRows = 4 * kDecUpCols;     // W_up tile rows (40): row 4 c + s
+constexpr int kStageItems = kDecDownCols / 4;  // float4 activation items per token (80)
+constexpr int kYRow = kDecDownCols + 8;     // padded LDS row of an activation plane (bf16)
+constexpr int kLoRow = kRank + 8;           // padded LDS row of a lo plane (bf16)
 // Scratch layout (in 64-bit words from the base): partial dots, slice sums of
 // squares, lo, then the 32-bit generation counters and the timeout counter.
 // Every producer writes whole 128-byte lines (16 words), padding unused token
 // slots: a line the XCD's L2 holds only in part is filled from memory when it
-// is read, which costs a memory round trip (about 0.5 us while the weights
-// stream) instead of an L2 hit.
-//   part [8 xcd][16 down wg][40 rows][8 tokens]     (two rows per line)
-//   ssq  [8 xcd][16 down wg][16]                    (tokens 0..7, then padding)
+// is read, which costs a memory round trip instead of an L2 hit.
+//   part [8 xcd][32 wg][40 rows][8 tokens]          (two rows per line)
+//   ssq  [8 xcd][32 wg][16]                         (tokens 0..7, then padding)
 //   lo   [8 replica][8 xcd][16 reducer] blocks of 64 words, the first 32 being
 //        [8 tokens][4 rows] (rows 3 u .. 3 u + 2, padding).  Each reducer writes
 //        one replica per consumer XCD, and the blocks are spread 512 bytes
-//        apart: every line is then read by the 16 up workgroups of one XCD,
-//        spread over many memory channels, instead of by all 128 at once.
+//        apart: every line is then read by the 32 workgroups of one XCD,
+//        spread over many memory channels, instead of by all 256 at once.
 constexpr int kSsqLine = 16;
 constexpr int kLoRows = 4;
 constexpr int kLoBlock = 64;
-constexpr size_t kPartWords = (size_t)kDecXcds * kDecDownPerXcd * kDecRowsPerXcd * kDecMaxT;
-constexpr size_t kSsqWords = (size_t)kDecXcds * kDecDownPerXcd * kSsqLine;
+constexpr size_t kPartWords = (size_t)kDecXcds * kDecWgPerXcd * kDecRowsPerXcd * kDecMaxT;
+constexpr size_t kSsqWords = (size_t)kDecXcds * kDecWgPerXcd * kSsqLine;
 constexpr size_t kLoWords = (size_t)kDecXcds * kDecXcds * 16 * kLoBlock;
 // word index of (token t, reducer row r) of reducer (xs, us) in replica y
 __host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
@@ -105,19 +106,18 @@ __host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
     return ((y * kDecXcds + xs) * 16 + us) * kLoBlock + t * kLoRows + r;
 }
 
-// LDS bytes per role: the weight tile, then the role's planes
-constexpr size_t down_lds(int T)
-{
-    return 16 * kTileChunks + 2 * 3 * T * kYRow + 4 * T * kStageItems + 6 * 2 * 64 * 16;
-}
-constexpr size_t up_lds(int T)
-{
-    return 16 * kTileChunks + 2 * 3 * T * kLoRow + 4 * T * kUpRows + (kDecUpCols / 4) * 2 * 64 * 16;
-}
-constexpr size_t lds_bytes(int T)
-{
-    return down_lds(T) > up_lds(T) ? down_lds(T) : up_lds(T);
-}
+// LDS map (bytes): both weight tiles, the y planes [3 T][kYRow] bf16, the
+// token sums of squares of the items [T][80] fp32, the down product blocks
+// [6][2 chains][64] f32x4, the lo planes [3 T][kLoRow] bf16, R' of the up
+// tile's rows [T][40] fp32, the up product blocks [3][2 chains][64] f32x4.
+constexpr size_t kOffUTile = 16 * kTileChunks;
+constexpr size_t kOffY = 2 * 16 * kTileChunks;
+template <int T> constexpr size_t kOffSs = kOffY + 2 * 3 * T * kYRow;
+template <int T> constexpr size_t kOffComb = kOffSs<T> + 4 * T * kStageItems;
+template <int T> constexpr size_t kOffLo = kOffComb<T> + 6 * 2 * 64 * 16;
+template <int T> constexpr size_t kOffRp = kOffLo<T> + 2 * 3 * T * kLoRow;
+template <int T> constexpr size_t kOffUComb = kOffRp<T> + 4 * T * kUpRows;
+template <int T> constexpr size_t kLdsBytes = kOffUComb<T> + 3 * 2 * 64 * 16;
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
 {
@@ -346,14 +346,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16)
 {
     static_assert(T >= 1 && T <= kDecMaxT, "short-window kernel takes 1..8 tokens");
-    static_assert(kDecRowsPerXcd * kDnRowChunks == kTileChunks && kUpRows * kUpRowChunks == kTileChunks,
-                  "both tiles are 3200 chunks");
-    static_assert(kWidth % kDecDownCols == 0, "a W_down tile lies in one stream");
-    static_assert(kDecXcds * kDecRowsPerXcd == kRank && kDecXcds * kDecUpPerXcd * kDecUpCols == kWidth, "cover");
-    static_assert(kStageItems * kDecMaxT <= 3 * kDecThreads && kUpRows * kDecMaxT <= 2 * kDecThreads, "passes");
-    static_assert(kDecReducers <= 16 && kDecRedRows <= 3 && kDecDownPerXcd == 16, "one reducer wave");
-    __shared__ __align__(16) uint4 lds[lds_bytes(T) / 16];
-    uint4* const tile = lds;  // the role's weight tile
+    static_assert(kDecRowsPerXcd * kRowChunks == kTileChunks && kUpRows * kRowChunks == kTileChunks,
+                  "both tiles are 1600 chunks");
+    static_assert(kWidth % kDecDownCols == 0 && kWidth / kDecDownCols == 8, "8 down tiles per stream");
+    static_assert(kDecXcds * kDecRowsPerXcd == kRank && kDecWGs * kDecUpCols == kWidth, "cover");
+    static_assert(kStageItems * kDecMaxT <= 2 * kDecThreads && kUpRows * kDecMaxT <= kDecThreads, "passes");
+    static_assert(kDecReducers <= 16 && kDecRedRows == 3 && kDecWgPerXcd == 32, "reducer layout");
+    static_assert(kLdsBytes<T> <= 160 * 1024, "LDS");
+    __shared__ __align__(16) uint4 lds[kLdsBytes<T> / 16];
+    uint4* const dtile = lds;                                                              // W_down tile
+    uint4* const utile = lds + kOffUTile / 16;                                             // W_up tile
+    uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kOffY / 16);                  // [3 T][kYRow]
+    float* const sspart = reinterpret_cast<float*>(lds + kOffSs<T> / 16);                 // [T][80]
+    f32x4_t* const comb = reinterpret_cast<f32x4_t*>(lds + kOffComb<T> / 16);             // [6][chains][64]
+    uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kOffLo<T> / 16);              // [3 T][kLoRow]
+    float* const rpl = reinterpret_cast<float*>(lds + kOffRp<T> / 16);                    // [T][40]
+    f32x4_t* const ucomb = reinterpret_cast<f32x4_t*>(lds + kOffUComb<T> / 16);           // [3][chains][64]
 
     DecodeScratch s;
     s.part = scratch;
@@ -363,15 +371,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     s.timeouts = s.gen + kDecWGs;
     const int b = blockIdx.x;
     const int x = b & 7;   // group (all its workgroups share one XCD)
-    const int i = b >> 3;  // index inside the XCD, 0..31
+    const int i = b >> 3;  // index inside the group, 0..31
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // MFMA column slot (B / D operand)
     const int g = lane >> 4;  // MFMA k-group (A / B operand) and D row group
-    const int m = lane & 15;  // MFMA A row = token
+    const int m = lane & 15;  // MFMA A row
+    const int k0 = kDecDownCols * i;                 // first W_down column (inside stream i / 8)
+    const int c0 = kDecUpCols * (kDecWgPerXcd * x + i);  // first output column
+    const bool reducer = i < kDecReducers;
+    const int u = i;                                 // reducer index: rows 3 u .. 3 u + 2 of the group
     // this launch's generation: one more than the launches this workgroup has
     // seen.  Every lane loads the counter (no per-lane branch); the value is
-    // used only after the weights have landed.
+    // used only after the W_down tile has landed.
     uint32_t seen = __hip_atomic_load(&s.gen[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The dispatcher deals workgroups to the XCDs round robin, starting where
     // the previous dispatch stopped: workgroup b runs on XCD (b + r) % 8 with
@@ -382,298 +394,307 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // (counted) wait, never as a silent stale read.
     const uint32_t rot = (__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) - (uint32_t)x) & 7u;
     HC_PROBE(0, threadIdx.x == 0);
-    // Loads issued before the first wait are unconditional (items past the end
-    // re-read item 0; a missing pending re-reads R): a conditional load makes
-    // the compiler merge registers, which waits for every load.
-    const float* Pm = P ? P : R;
+    const float* const Pm = P ? P : R;  // (a missing pending re-reads R)
 
-    if (i < kDecDownPerXcd) {
-        // =========================== down ===========================
-        const int d = i;
-        uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kTileChunks);     // [3][T][kYRow]
-        float* const sspart = reinterpret_cast<float*>(ypl + 3 * T * kYRow);       // [T][160]
-        f32x4_t* const comb = reinterpret_cast<f32x4_t*>(sspart + T * kStageItems);  // [6][chains][64]
-
-        // (1) the W_down tile: rows 40 x + row, columns 640 d + 8 j ..
-        for (int q = wave; q < kTileInstr; q += 8) {
-            int row, j;
-            tile_lane<kDnRowChunks>(q, lane, row, j);
-            dma16(W_down + (size_t)(kDecRowsPerXcd * x + row) * kD + kDecDownCols * d + 8 * j, tile + 64 * q);
-        }
-        // the activations of columns [640 d, 640 d + 640)
-        float4 rv[3], pv[3], wv[3];
-#pragma unroll
-        for (int pass = 0; pass < 3; ++pass) {
-            const int it = threadIdx.x + kDecThreads * pass;
-            const int itc = it < kStageItems * T ? it : 0;
-            const int at = itc / kStageItems, f = itc - at * kStageItems;
-            const size_t o = (size_t)at * kD + kDecDownCols * d + 4 * f;
-            rv[pass] = *reinterpret_cast<const float4*>(R + o);
-            pv[pass] = *reinterpret_cast<const float4*>(Pm + o);
-            wv[pass] = *reinterpret_cast<const float4*>(w_norm + kDecDownCols * d + 4 * f);
-        }
-        // (2) y = R' * w_norm (unscaled: the norm is folded into the
-        //     reduction), its sums of squares, and the exact 3-way split
-#pragma unroll
-        for (int pass = 0; pass < 3; ++pass) {
-            const int it = threadIdx.x + kDecThreads * pass;
-            if (it < kStageItems * T) {
-                const int at = it / kStageItems, f = it - at * kStageItems;
-                const float r[4] = {P ? rv[pass].x + pv[pass].x : rv[pass].x, P ? rv[pass].y + pv[pass].y : rv[pass].y,
-                                    P ? rv[pass].z + pv[pass].z : rv[pass].z, P ? rv[pass].w + pv[pass].w : rv[pass].w};
-                const float w[4] = {wv[pass].x, wv[pass].y, wv[pass].z, wv[pass].w};
-                float ss = 0.f;
-                uint32_t hi[4], mi[4], lo[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ss += r[e] * r[e];
-                    split3(r[e] * w[e], hi[e], mi[e], lo[e]);
-                }
-                sspart[at * kStageItems + f] = ss;
-                const int col = 4 * f;
-                *reinterpret_cast<uint2*>(&ypl[(0 * T + at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-                *reinterpret_cast<uint2*>(&ypl[(1 * T + at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-                *reinterpret_cast<uint2*>(&ypl[(2 * T + at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-            }
-        }
-        wait_all_loads();  // this wave's part of the tile is in LDS
-        wg_barrier();      // B1: activations staged, W_down tile complete
-        HC_PROBE(1, threadIdx.x == 0);
-        pin(seen);
-        const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
-
-        // (3) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
-        //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over
-        //     K steps 10 (w / 3) .. +9 of 32 columns.  A rows are (piece,
-        //     token) pairs in the planes' own order (row p T + t: piece p of
-        //     token t), so one chain of MFMAs carries all three pieces when
-        //     3 T <= 16, two chains (pieces 0-1, then piece 2) otherwise.
-        if (wave < 6) {
-            const int nb = wave % 3, kh = wave / 3;
-            const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
-            // all operands first (one LDS latency, not ten); A rows past the
-            // pieces re-read row 0: they only feed D rows nobody reads
-            const int r0 = m < kPackRows<T> ? m : 0;
-            const int r1 = 2 * T + (m < T ? m : 0);
-            uint4 wb[10], a0[10], a1[10];
-#pragma unroll
-            for (int qq = 0; qq < 10; ++qq) {
-                const int q = 10 * kh + qq;
-                const int col = 32 * q + 8 * g;
-                wb[qq] = tile[tile_pos<kDnRowChunks>(row, 4 * q + g)];
-                a0[qq] = *reinterpret_cast<const uint4*>(&ypl[r0 * kYRow + col]);
-                if (kChains<T> == 2)
-                    a1[qq] = *reinterpret_cast<const uint4*>(&ypl[r1 * kYRow + col]);
-            }
-            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-            for (int qq = 0; qq < 10; ++qq) {
-                acc0 = mfma16(a0[qq], wb[qq], acc0);
-                if (kChains<T> == 2)
-                    acc1 = mfma16(a1[qq], wb[qq], acc1);
-            }
-            comb[(wave * kChains<T>) * 64 + lane] = acc0;
-            if (kChains<T> == 2)
-                comb[(wave * kChains<T> + 1) * 64 + lane] = acc1;
-        } else if (wave == 6) {
-            // (3') meanwhile, the slice's sum of squares per token: lane 8 t + p
-            //      sums 20 of token t's 160 item sums, then the 8 lanes combine theirs
-            const int tt = lane >> 3, p = lane & 7;
-            float ss = 0.f;
-            if (tt < T) {
-#pragma unroll
-                for (int f = 0; f < 20; ++f)
-                    ss += sspart[tt * kStageItems + 20 * p + f];
-            }
-            ss = sum8(ss);
-            if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
-                st_word_xcd(&s.ssq[((size_t)x * kDecDownPerXcd + d) * kSsqLine + 8 * p + tt],
-                            tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
-        }
-        HC_PROBE(2, threadIdx.x == 0);
-        wg_barrier();  // Bc1: every product block in LDS
-
-        if (wave < 6) {
-            // (4) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g,
-            //     into the XCD's L2: per K half hi + (mid + lo3), then the two
-            //     halves (all 8 token slots, whole lines; slots >= T hold 0)
-            const float* cf = reinterpret_cast<const float*>(comb);
-            const int nb = wave % 3, t = 4 * (wave / 3) + g;
-            const int row = 16 * nb + n;
-            if (row < kDecRowsPerXcd) {
-                const float v = t < T ? piece_sum<T>(cf, nb, t, n) + piece_sum<T>(cf, nb + 3, t, n) : 0.f;
-                st_word_xcd(s.part + (((size_t)x * kDecDownPerXcd + d) * kDecRowsPerXcd + row) * kDecMaxT + t,
-                            tag_f32(v, xcd_tag(gen, rot)));
-            }
-        }
-        HC_PROBE(3, threadIdx.x == 0);
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&s.gen[b], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-
-    // ============================= up =============================
-    const int u = i - kDecDownPerXcd;
-    const int c0 = kDecUpCols * (kDecUpPerXcd * x + u);  // first output column
-    uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kTileChunks);  // [3][T][kLoRow]
-    float* const rpl = reinterpret_cast<float*>(lpl + 3 * T * kLoRow);      // [T][80]: R' of tile row 20 s + r
-    f32x4_t* const ucomb = reinterpret_cast<f32x4_t*>(rpl + T * kUpRows);   // [5 waves][chains][64]
-
-    // (1) the W_up tile: rows s * 2560 + c0 + r (tile row 20 s + r)
+    // ---- Loads.  The W_down tile, the activations of its columns and the
+    //      poll-line touches come first; the W_up tile and R' of its rows are
+    //      issued only after this workgroup's down work (and, for a reducer,
+    //      after hop 1).  While loads into LDS are in flight the compiler makes
+    //      every LDS access wait for them, and a CU answers a poll only after
+    //      its own earlier loads: the second tile's loads must not overlap
+    //      either.  Loads issued before the first wait are unconditional
+    //      (items past the end re-read item 0): a conditional load makes the
+    //      compiler merge registers, which waits.
+    // (1) W_down tile: rows 40 x + row, columns k0 + 8 j ..
     for (int q = wave; q < kTileInstr; q += 8) {
         int row, j;
-        tile_lane<kUpRowChunks>(q, lane, row, j);
-        const int k = (row / kDecUpCols) * kWidth + c0 + row % kDecUpCols;
-        dma16(W_up + (size_t)k * kRank + 8 * j, tile + 64 * q);
+        tile_lane<kRowChunks>(q, lane, row, j);
+        dma16(W_down + (size_t)(kDecRowsPerXcd * x + row) * kD + k0 + 8 * j, dtile + 64 * q);
     }
-    // (2) a reducer touches (plain loads, which keep the lines in this XCD's
-    //     L2) the lines it will poll: the 16 producers' partial rows
-    //     3 u .. 3 u + 2 and their sums of squares.  Polls then hit L2 and see
-    //     a producer's store as soon as it lands, instead of each round
-    //     fetching the line from memory.  (Only lines written inside this XCD
-    //     are touched this way.)  The loaded value is consumed only after the
-    //     weights have landed, so nothing waits for it before then.
-    uint32_t touched = 0;
-    if (wave == 0 && u < kDecReducers) {
-        const int src = lane & 15, k = lane >> 4;  // k 0..2: partial lines, 3: sums of squares
-        const int rowl = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
-        const uint64_t* line = k < 3 ? s.part + (((size_t)x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowl) * kDecMaxT
-                                     : s.ssq + ((size_t)x * kDecDownPerXcd + src) * kSsqLine;
-        touched = *reinterpret_cast<const uint32_t*>(line);  // (not volatile: that would wait here)
-    }
-    // R and pending of the same 80 (stream, column) pairs, for the mix
-    float mr[2], mp[2];
+    // (2) the activations of columns [k0, k0 + 320)
+    constexpr int kItems = kStageItems * T;
+    constexpr int kPasses = (kItems + kDecThreads - 1) / kDecThreads;
+    float4 rv[kPasses], pv[kPasses], wv[kPasses];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
         const int it = threadIdx.x + kDecThreads * pass;
+        const int itc = it < kItems ? it : 0;
+        const int at = itc / kStageItems, f = itc - at * kStageItems;
+        const size_t o = (size_t)at * kD + k0 + 4 * f;
+        rv[pass] = *reinterpret_cast<const float4*>(R + o);
+        pv[pass] = *reinterpret_cast<const float4*>(Pm + o);
+        wv[pass] = *reinterpret_cast<const float4*>(w_norm + k0 + 4 * f);
+    }
+    // (3) a reducer touches (plain loads, which keep the lines in this XCD's
+    //     L2) the lines it will poll: the 32 producers' partial rows 3 u ..
+    //     3 u + 2 and their sums of squares.  Polls then hit L2 and see a
+    //     producer's store as soon as it lands, instead of each round
+    //     fetching the line from memory.
+    uint32_t touched = 0, touched2 = 0;
+    if (wave == 0 && reducer) {
+        const int src = lane & 31, k = lane >> 5;  // k 0, 1: partial lines of rows 3 u and 3 u + 2
+        const int row = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
+        touched = *reinterpret_cast<const uint32_t*>(
+            s.part + (((size_t)x * kDecWgPerXcd + src) * kDecRowsPerXcd + row) * kDecMaxT);
+        touched2 = *reinterpret_cast<const uint32_t*>(s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
+    }
+    // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
+    //     and R and pending of those 40 (stream, column) pairs, for the mix
+    float mr = 0.f, mp = 0.f;
+    auto issue_up = [&]() {
+        for (int q = wave; q < kTileInstr; q += 8) {
+            int row, j;
+            tile_lane<kRowChunks>(q, lane, row, j);
+            dma16(W_up + (size_t)((row & 3) * kWidth + c0 + (row >> 2)) * kRank + 8 * j, utile + 64 * q);
+        }
+        const int it = threadIdx.x;
         const int itc = it < kUpRows * T ? it : 0;
         const int at = itc / kUpRows, row = itc - at * kUpRows;
-        const size_t o = (size_t)at * kD + (row / kDecUpCols) * kWidth + c0 + row % kDecUpCols;
-        mr[pass] = R[o];
-        mp[pass] = Pm[o];
-    }
+        const size_t o = (size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2);
+        mr = R[o];
+        mp = Pm[o];
+    };
+
+    // (6) y = R' * w_norm (unscaled: the norm is folded into the reduction),
+    //     its sums of squares, and the exact 3-way split
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
         const int it = threadIdx.x + kDecThreads * pass;
-        if (it < kUpRows * T)
-            rpl[it] = P ? mr[pass] + mp[pass] : mr[pass];  // it = 80 t + row
+        if (it < kItems) {
+            const int at = it / kStageItems, f = it - at * kStageItems;
+            float ss = 0.f;
+            uint32_t hi[4], mi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float rvv[4] = {rv[pass].x, rv[pass].y, rv[pass].z, rv[pass].w};
+                const float pvv[4] = {pv[pass].x, pv[pass].y, pv[pass].z, pv[pass].w};
+                const float wvv[4] = {wv[pass].x, wv[pass].y, wv[pass].z, wv[pass].w};
+                const float r = P ? rvv[e] + pvv[e] : rvv[e];
+                ss += r * r;
+                split3(r * wvv[e], hi[e], mi[e], lo[e]);
+            }
+            sspart[at * kStageItems + f] = ss;
+            const int col = 4 * f;
+            *reinterpret_cast<uint2*>(&ypl[(0 * T + at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(&ypl[(1 * T + at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
+            *reinterpret_cast<uint2*>(&ypl[(2 * T + at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
     }
-    wait_all_loads();  // every load of this CU has landed: from here on, hand-off loads run at cache latency
-    asm volatile("" ::"v"(touched));
-    wg_barrier();      // B1
+    wait_all_loads();  // this wave's part of the W_down tile is in LDS
+    asm volatile("" ::"v"(touched), "v"(touched2));
+    wg_barrier();      // B1: y staged, W_down tile complete
     HC_PROBE(1, threadIdx.x == 0);
     pin(seen);
     const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
 
-    if (wave == 0) {
-        if (u < kDecReducers) {
-            // (5) hop 1: lo rows 3 u .. 3 u + 2 of this XCD from its 16
-            //     down workgroups' partials, each stream's rs from its 4
-            //     slices' sums of squares; lo published device-wide.  Up to 4
-            //     tokens, a lane group per row (rows in parallel, tokens in
-            //     turn); from 5 tokens, a lane group per pair of tokens (one
-            //     load per row per polling round, rows in turn).
-            if constexpr (T <= 4) {
-                // lane = src + 16 r: row 3 u + r (r < 3) of down workgroup src
-                const int r = lane >> 4, src = lane & 15;
-                const int row = kDecRedRows * u + r;
-                const bool valid = r < kDecRedRows && row < kDecRowsPerXcd;
-                const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
-                const int pidx = ((x * kDecDownPerXcd + src) * kDecRowsPerXcd + rowc) * kDecMaxT;
-                const int sidx = (x * kDecDownPerXcd + src) * kSsqLine;
-                const long long t0 = wall_clock64();
-                float v[T], q[T];
-                poll_words<T>(s.part, pidx, s.ssq, sidx, xcd_tag(gen, rot), t0, lane, v, q, s.timeouts, 0);
-                HC_PROBE(12, lane == 0);
-                float mine = 0.f;  // lo of row 3 u + r, token `src`
+    // (7) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
+    //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over K
+    //     steps 5 (w / 3) .. +4 of 32 columns.  A rows are (piece, token)
+    //     pairs in the planes' own order (row p T + t: piece p of token t), so
+    //     one chain of MFMAs carries all three pieces when 3 T <= 16, two
+    //     chains (pieces 0-1, then piece 2) otherwise.
+    if (wave < 6) {
+        const int nb = wave % 3, kh = wave / 3;
+        const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
+        // all operands first (one LDS latency, not five); A rows past the
+        // pieces re-read row 0: they only feed D rows nobody reads
+        const int r0 = m < kPackRows<T> ? m : 0;
+        const int r1 = 2 * T + (m < T ? m : 0);
+        uint4 wb[5], a0[5], a1[5];
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
-                    const float ss = sum4(q[t]);
-                    const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
-                    const float y = sum4(v[t]) * rs;
-                    const float y01 = y + dpp<0x141>(y);      // row_half_mirror: (s0 + s1), (s2 + s3)
-                    const float lo = y01 + dpp<0x140>(y01);   // row_mirror: (s0 + s1) + (s2 + s3)
-                    if (src == t)
-                        mine = lo;
-                }
-                // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
-                // this reducer, 0 in the padding
-                const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
+        for (int qq = 0; qq < 5; ++qq) {
+            const int q = 5 * kh + qq;
+            const int col = 32 * q + 8 * g;
+            wb[qq] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
+            a0[qq] = *reinterpret_cast<const uint4*>(&ypl[r0 * kYRow + col]);
+            if (kChains<T> == 2)
+                a1[qq] = *reinterpret_cast<const uint4*>(&ypl[r1 * kYRow + col]);
+        }
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-                for (int y = 0; y < kDecXcds; ++y)
-                    if (src < kDecMaxT)
-                        st_word(&s.lo[lo_word(y, x, u, src, r)], word);
-            } else {
-                // lane = src + 16 q: tokens 2 q, 2 q + 1 of down workgroup src
-                // (a polling round is 3 row loads and 1 sum-of-squares load)
-                const int src = lane & 15, q = lane >> 4;
-                const int pbase = (x * kDecDownPerXcd + src) * kDecRowsPerXcd;
-                int pidx[kDecRedRows];
+        for (int qq = 0; qq < 5; ++qq) {
+            acc0 = mfma16(a0[qq], wb[qq], acc0);
+            if (kChains<T> == 2)
+                acc1 = mfma16(a1[qq], wb[qq], acc1);
+        }
+        comb[(wave * kChains<T>) * 64 + lane] = acc0;
+        if (kChains<T> == 2)
+            comb[(wave * kChains<T> + 1) * 64 + lane] = acc1;
+    } else if (wave == 6) {
+        // (7') meanwhile, the slice's sum of squares per token: lane 8 t + p
+        //      sums 10 of token t's 80 item sums, then the 8 lanes combine theirs
+        const int tt = lane >> 3, p = lane & 7;
+        float ss = 0.f;
+        if (tt < T) {
 #pragma unroll
-                for (int rr = 0; rr < kDecRedRows; ++rr) {
-                    const int row = kDecRedRows * u + rr;
-                    pidx[rr] = (pbase + (row < kDecRowsPerXcd ? row : kDecRowsPerXcd - 1)) * kDecMaxT + 2 * q;
-                }
-                const int sidx = (x * kDecDownPerXcd + src) * kSsqLine + 2 * q;
-                const uint32_t htag = xcd_tag(gen, rot);
-                const long long t0 = wall_clock64();
-                uint4 pw[kDecRedRows], sw;
-                [[maybe_unused]] int rounds = 0;
-                while (true) {
-                    ++rounds;
-                    new_round();
-#pragma unroll
-                    for (int rr = 0; rr < kDecRedRows; ++rr)
-                        pw[rr] = ld_words2(s.part, pidx[rr]);
-                    sw = ld_words2(s.ssq, sidx);
-                    bool ok = sw.y == htag && sw.w == htag;
-#pragma unroll
-                    for (int rr = 0; rr < kDecRedRows; ++rr)
-                        ok = ok && pw[rr].y == htag && pw[rr].w == htag;
-                    if (__all(ok)) {
-                        HC_COUNT(0, 0, rounds, lane == 0);
-                        break;
-                    }
-                    if (wall_clock64() - t0 > kWaitTicks) {
-                        if (lane == 0)
-                            note_timeout(s.timeouts);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                HC_PROBE(12, lane == 0);
-                float lo[kDecRedRows][2];  // [row][token 2 q + h], the same in all 16 lanes of q
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    // lanes 4 s .. 4 s + 3 (of each 16) hold the slices of stream s
-                    const float ss = sum4(__uint_as_float(h ? sw.z : sw.x));
-                    const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
-#pragma unroll
-                    for (int rr = 0; rr < kDecRedRows; ++rr) {
-                        const float y = sum4(__uint_as_float(h ? pw[rr].z : pw[rr].x)) * rs;
-                        const float y01 = y + dpp<0x141>(y);     // row_half_mirror: (s0 + s1), (s2 + s3)
-                        lo[rr][h] = y01 + dpp<0x140>(y01);       // row_mirror: (s0 + s1) + (s2 + s3)
-                    }
-                }
-                // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
-                // this reducer, 0 in the padding; lane src < 8 of q writes row
-                // src / 2, token 2 q + src % 2
-                const int rr = src >> 1, h = src & 1, tok = 2 * q + h;
-                const float mine = rr == 0 ? lo[0][h] : rr == 1 ? lo[1][h] : lo[2][h];
-                const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
-                const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
-#pragma unroll
-                for (int y = 0; y < kDecXcds; ++y)
-                    if (src < 8)
-                        st_word(&s.lo[lo_word(y, x, u, tok, rr)], word);
-            }
-            HC_PROBE(13, lane == 0);
+            for (int f = 0; f < kStageItems / 8; ++f)
+                ss += sspart[tt * kStageItems + (kStageItems / 8) * p + f];
+        }
+        ss = sum8(ss);
+        if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
+            st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + 8 * p + tt],
+                        tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
+    }
+    HC_PROBE(2, threadIdx.x == 0);
+    wg_barrier();  // Bc1: every product block in LDS
+
+    if (wave < 6) {
+        // (8) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g, into
+        //     the XCD's L2: per K half hi + (mid + lo3), then the two halves
+        //     (all 8 token slots, whole lines; slots >= T hold 0)
+        const float* cf = reinterpret_cast<const float*>(comb);
+        const int nb = wave % 3, t = 4 * (wave / 3) + g;
+        const int row = 16 * nb + n;
+        if (row < kDecRowsPerXcd) {
+            const float v = t < T ? piece_sum<T>(cf, nb, t, n) + piece_sum<T>(cf, nb + 3, t, n) : 0.f;
+            st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kDecMaxT + t,
+                        tag_f32(v, xcd_tag(gen, rot)));
         }
     }
-    wg_barrier();  // Bs
+    HC_PROBE(3, threadIdx.x == 0);
+
+    if (!reducer)
+        issue_up();
+
+    if (wave == 0 && reducer) {
+        // (9) hop 1: lo rows 3 u .. 3 u + 2 of this group from its 32
+        //     workgroups' partials, each stream's rs from its 8 slices' sums
+        //     of squares; lo published device-wide.  Lane src + 16 k holds
+        //     sources src (streams 0-1) and src + 16 (streams 2-3); within
+        //     each 16 lanes, lanes 8 s' .. 8 s' + 7 hold the 8 slices of
+        //     streams s' and s' + 2.  Up to 4 tokens, lane group k = row
+        //     (rows in parallel, tokens in turn); from 5 tokens, k = pair of
+        //     tokens (one load per row and source per polling round).
+        const uint32_t htag = xcd_tag(gen, rot);
+        const long long t0 = wall_clock64();
+        const int src = lane & 15, k = lane >> 4;
+        const int pa0 = (x * kDecWgPerXcd + src) * kDecRowsPerXcd, pb0 = pa0 + 16 * kDecRowsPerXcd;
+        const int sa0 = (x * kDecWgPerXcd + src) * kSsqLine, sb0 = sa0 + 16 * kSsqLine;
+        // lo of (stream pair sums) -> (s0 + s1) + (s2 + s3), the same in all 16 lanes
+        auto combine = [](float pa, float pb, float qa, float qb) {
+            const float rsa = rsqrtf(sum8(qa) * (1.0f / (float)kWidth) + kEps);
+            const float rsb = rsqrtf(sum8(qb) * (1.0f / (float)kWidth) + kEps);
+            const float ya = sum8(pa) * rsa, yb = sum8(pb) * rsb;
+            const float za = ya + dpp<0x140>(ya);  // row_mirror: the other half's stream
+            const float zb = yb + dpp<0x140>(yb);
+            return za + zb;
+        };
+        if constexpr (T <= 4) {
+            constexpr int NP = (T + 1) / 2;
+            const int row = kDecRedRows * u + k;
+            const bool valid = k < kDecRedRows && row < kDecRowsPerXcd;
+            const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
+            const int pa = (pa0 + rowc) * kDecMaxT, pb = (pb0 + rowc) * kDecMaxT;
+            uint4 wa_[NP], wb_[NP], qa_[NP], qb_[NP];
+            [[maybe_unused]] int rounds = 0;
+            while (true) {
+                ++rounds;
+                new_round();
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    wa_[q] = ld_words2(s.part, pa + 2 * q);
+                    wb_[q] = ld_words2(s.part, pb + 2 * q);
+                    qa_[q] = ld_words2(s.ssq, sa0 + 2 * q);
+                    qb_[q] = ld_words2(s.ssq, sb0 + 2 * q);
+                }
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    ok = ok & (wa_[q].y == htag) & (wb_[q].y == htag) & (qa_[q].y == htag) & (qb_[q].y == htag) &
+                         (2 * q + 1 >= T || ((wa_[q].w == htag) & (wb_[q].w == htag) & (qa_[q].w == htag) &
+                                             (qb_[q].w == htag)));
+                if (__all(ok)) {
+                    HC_COUNT(0, 0, rounds, lane == 0);
+                    break;
+                }
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    if (lane == 0)
+                        note_timeout(s.timeouts);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            HC_PROBE(12, lane == 0);
+            float mine = 0.f;  // lo of row 3 u + k, token `src`
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const bool hi = t & 1;
+                const float lo = combine(__uint_as_float(hi ? wa_[t >> 1].z : wa_[t >> 1].x),
+                                         __uint_as_float(hi ? wb_[t >> 1].z : wb_[t >> 1].x),
+                                         __uint_as_float(hi ? qa_[t >> 1].z : qa_[t >> 1].x),
+                                         __uint_as_float(hi ? qb_[t >> 1].z : qb_[t >> 1].x));
+                if (src == t)
+                    mine = lo;
+            }
+            // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
+            // this reducer, 0 in the padding; lane src < 8 of group k writes
+            // row k, token src
+            const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
+#pragma unroll
+            for (int y = 0; y < kDecXcds; ++y)
+                if (src < kDecMaxT)
+                    st_word(&s.lo[lo_word(y, x, u, src, k)], word);
+        } else {
+            int pidx[kDecRedRows];
+#pragma unroll
+            for (int rr = 0; rr < kDecRedRows; ++rr) {
+                const int row = kDecRedRows * u + rr;
+                pidx[rr] = (row < kDecRowsPerXcd ? row : kDecRowsPerXcd - 1) * kDecMaxT + 2 * k;
+            }
+            uint4 wa_[kDecRedRows], wb_[kDecRedRows], qa_, qb_;
+            [[maybe_unused]] int rounds = 0;
+            while (true) {
+                ++rounds;
+                new_round();
+#pragma unroll
+                for (int rr = 0; rr < kDecRedRows; ++rr) {
+                    wa_[rr] = ld_words2(s.part, pa0 * kDecMaxT + pidx[rr]);
+                    wb_[rr] = ld_words2(s.part, pb0 * kDecMaxT + pidx[rr]);
+                }
+                qa_ = ld_words2(s.ssq, sa0 + 2 * k);
+                qb_ = ld_words2(s.ssq, sb0 + 2 * k);
+                bool ok = (qa_.y == htag) & (qa_.w == htag) & (qb_.y == htag) & (qb_.w == htag);
+#pragma unroll
+                for (int rr = 0; rr < kDecRedRows; ++rr)
+                    ok = ok & (wa_[rr].y == htag) & (wa_[rr].w == htag) & (wb_[rr].y == htag) & (wb_[rr].w == htag);
+                if (__all(ok)) {
+                    HC_COUNT(0, 0, rounds, lane == 0);
+                    break;
+                }
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    if (lane == 0)
+                        note_timeout(s.timeouts);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            HC_PROBE(12, lane == 0);
+            float lo[kDecRedRows][2];  // [row][token 2 k + h], the same in all 16 lanes of k
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int rr = 0; rr < kDecRedRows; ++rr)
+                    lo[rr][h] = combine(__uint_as_float(h ? wa_[rr].z : wa_[rr].x),
+                                        __uint_as_float(h ? wb_[rr].z : wb_[rr].x),
+                                        __uint_as_float(h ? qa_.z : qa_.x), __uint_as_float(h ? qb_.z : qb_.x));
+            // lane src < 8 of group k writes row src / 2, token 2 k + src % 2
+            const int rr = src >> 1, h = src & 1, tok = 2 * k + h;
+            const float l0 = h ? lo[0][1] : lo[0][0], l1 = h ? lo[1][1] : lo[1][0], l2 = h ? lo[2][1] : lo[2][0];
+            const float mine = rr == 0 ? l0 : rr == 1 ? l1 : l2;
+            const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
+            const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
+#pragma unroll
+            for (int y = 0; y < kDecXcds; ++y)
+                if (src < 8)
+                    st_word(&s.lo[lo_word(y, x, u, tok, rr)], word);
+        }
+        HC_PROBE(13, lane == 0);
+    }
+    wg_barrier();  // Bs: this workgroup's hop 1 done
+    if (reducer)
+        issue_up();
     {
-        // (6) hop 2: wave w polls the lo words of XCD w's reducers (slot =
+        // (10) hop 2: wave w polls the lo words of XCD w's reducers (slot =
         //     reducer, token, pair of rows) until every tag is current, then
         //     stages the 3 bf16 pieces of each value.  (Waves start after this
         //     workgroup's own reducer is done, so their cold loads do not
@@ -736,23 +757,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
         HC_PROBE(7, wave == 0 && lane == 0);
     }
-    wg_barrier();  // B2: lo staged
+    wait_all_loads();  // the W_up tile and R' have landed
+    if (threadIdx.x < kUpRows * T)
+        rpl[threadIdx.x] = P ? mr + mp : mr;  // it = 40 t + row
+    wg_barrier();  // B2: lo and R' staged, W_up tile complete
     HC_PROBE(8, threadIdx.x == 0);
 
-    if (wave < kDecUpCols / 4) {
-        // (7) up projection: wave w < 5 takes output columns c0 + 4 w .. +3
-        //     (slot n = 4 column + stream), all 10 K steps, A rows packed as
-        //     in the down projection; gated = up (identity epilogue); then the
-        //     mix of the 4 streams of a column
-        const int cc = n >> 2, st = n & 3;
-        const int row = st * kDecUpCols + 4 * wave + cc;
+    if (wave < 3) {
+        // (11) up projection: wave w < 3 takes tile rows 16 w .. +15 (slot n =
+        //      4 column + stream; block 2: rows 32..39, its upper 8 slots
+        //      repeat them), all 10 K steps, A rows packed as in the down
+        //      projection; gated = up (identity epilogue); then the mix of the
+        //      4 streams of a column
+        const int row = wave < 2 ? 16 * wave + n : 32 + (n & 7);
+        const int st = n & 3;
         const int r0 = m < kPackRows<T> ? m : 0;
         const int r1 = 2 * T + (m < T ? m : 0);
         uint4 wb[10], a0[10], a1[10];
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             const int jc = 32 * q + 8 * g;
-            wb[q] = tile[tile_pos<kUpRowChunks>(row, 4 * q + g)];
+            wb[q] = utile[tile_pos<kRowChunks>(row, 4 * q + g)];
             a0[q] = *reinterpret_cast<const uint4*>(&lpl[r0 * kLoRow + jc]);
             if (kChains<T> == 2)
                 a1[q] = *reinterpret_cast<const uint4*>(&lpl[r1 * kLoRow + jc]);
@@ -771,14 +796,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             ub[64 + lane] = acc1;
         asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
         const float* cf = reinterpret_cast<const float*>(ub);
-        const int c = c0 + 4 * wave + cc;
+        const int c = c0 + (row >> 2);
+        const bool owner = st == 0 && (wave < 2 || n < 8);  // (block 2's upper slots are copies)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tt = 4 * g + e;
             const float up = tt < T ? piece_sum<T>(cf, 0, tt, n) : 0.f;
             const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
             const float mixed = sum4(up * rp);  // (s0 + s1) + (s2 + s3)
-            if (st == 0 && tt < T) {
+            if (owner && tt < T) {
                 const size_t o = (size_t)tt * kWidth + c;
                 out_mixed[o] = mixed;
                 out_bf16[o] = __builtin_bit_cast(uint16_t, (__bf16)mixed);

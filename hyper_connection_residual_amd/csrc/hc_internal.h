@@ -18,35 +18,32 @@ constexpr float kEps = 1e-6f;
 // per CU, each of 8 waves.  Workgroup b belongs to group x = b % 8, i = b / 8;
 // the dispatcher deals workgroups to the 8 XCDs round robin, so the 32
 // workgroups of a group share one XCD and its L2 (the kernel checks it).
-// Each XCD's 32 workgroups split into two roles, so that no CU polls while
-// its own weight loads are in flight:
-//   down (i < 16, d = i): W_down rows [40 x, 40 x + 40) x columns
-//     [640 d, 640 d + 640) (inside stream d / 4); the partial dots and the
-//     slice's sum of squares go into the XCD's L2; then the workgroup ends;
-//   up (i >= 16, u = i - 16): W_up rows of output columns
-//     [20 (16 x + u), +20), all 4 streams.  Once they have landed, up
-//     workgroups u < 14 each reduce 3 rows of the XCD's 40 (hop 1, inside the
-//     XCD) and publish lo device-wide; every up workgroup then gathers all of
-//     lo (hop 2), runs the up projection and the stream mix.
+// Every workgroup takes two tiles of 25.6 KB, loaded in this order:
+//   down: W_down rows [40 x, 40 x + 40) x columns [320 i, 320 i + 320)
+//     (inside stream i / 8); its partial dots and the slice's sum of squares
+//     go into the XCD's L2;
+//   up: the W_up rows of output columns [10 (32 x + i), +10), all 4 streams.
+// Workgroups i < 14 of each group then reduce 3 of its 40 rows over the 32
+// partials (hop 1, inside the XCD) and publish lo device-wide; every
+// workgroup gathers all of lo (hop 2), runs the up projection and the mix.
 // Weight tiles are loaded straight into LDS as whole cache lines.  Hand-off
-// words are 64 bits: payload plus the launch's generation number, written
-// once with one store and polled by the consumer.
+// words are 64 bits: payload plus a tag, written once with one store and
+// polled by the consumer.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 8;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;
-constexpr int kDecDownPerXcd = 16;                               // down workgroups per XCD
-constexpr int kDecUpPerXcd = 16;                                 // up workgroups per XCD
+constexpr int kDecWgPerXcd = kDecWGs / kDecXcds;                 // 32 workgroups per XCD
 constexpr int kDecRowsPerXcd = kRank / kDecXcds;                 // 40 lo rows per XCD
-constexpr int kDecDownCols = kD / kDecDownPerXcd;                // 640 W_down columns per down workgroup
-constexpr int kDecUpCols = kWidth / (kDecXcds * kDecUpPerXcd);   // 20 output columns per up workgroup
-constexpr int kDecRedRows = 3;                                   // lo rows each reducing up workgroup reduces
+constexpr int kDecDownCols = kD / kDecWgPerXcd;                  // 320 W_down columns per workgroup
+constexpr int kDecUpCols = kWidth / kDecWGs;                     // 10 output columns per workgroup
+constexpr int kDecRedRows = 3;                                   // lo rows each reducing workgroup reduces
 constexpr int kDecReducers = (kDecRowsPerXcd + kDecRedRows - 1) / kDecRedRows;  // 14 per XCD
 
 struct DecodeScratch {
-    uint64_t* part;      // [8 xcd][16 down wg][40 rows][kDecMaxT]: partial dots (XCD-local)
-    uint64_t* ssq;       // [8 xcd][16 down wg][kDecMaxT]: column-slice sums of squares (XCD-local)
+    uint64_t* part;      // [8 xcd][32 wg][40 rows][kDecMaxT]: partial dots (XCD-local)
+    uint64_t* ssq;       // [8 xcd][32 wg][16]: column-slice sums of squares (XCD-local)
     uint64_t* lo;        // [kDecMaxT][kRank]: lo (device-wide)
     uint32_t* gen;       // [kDecWGs]: launches completed by each workgroup
     uint32_t* timeouts;  // [1]: expired bounded waits (a workgroup off its group's XCD expires one)
