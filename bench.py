@@ -11,8 +11,9 @@ on the next weight set).  Inputs are resident in HBM before timing starts.
 Prints ONE JSON line.  `value` = weight bytes streamed per second over the
 timed sweeps (GB/s), one hc_read call per read; the same sweeps replayed from
 captured HIP graphs (one graph per step) are reported under `graph`.  Per-T
-microseconds per read and the prefill read times are reported beside it.  The roofline object describes the short-window
-kernel; the CPU baseline is the plain oracle on the host.
+microseconds per read, the times of windows of 9..64 tokens and the prefill
+read times are reported beside it.  The roofline object describes the
+short-window kernel; the CPU baseline is the plain oracle on the host.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ TOKEN_BYTES_P = 4 * 2560 * 4 * 2 + 2560 * (4 + 2 + 2)  # R and pending read, mix
 HBM_PEAK_GBPS = 8000.0
 N_SETS = 48
 TS = list(range(1, 9))
+WINDOWS = [9, 12, 16, 24, 32, 33, 48, 64]  # windows above 8 tokens, timed beside the sweep
 
 
 def parse():
@@ -172,6 +174,31 @@ def main():
     print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
     del step_graphs
 
+    # ---- windows of 9..64 tokens (up to 32: one short-window launch per 8
+    # tokens; beyond: the wide path), eager, weights rotated over the 48 sets
+    from hyper_connection_residual_amd import workloads as wl
+    us_windows = {}
+    for T in WINDOWS:
+        rng = np.random.default_rng((1, 2000 + T))
+        R = torch.from_numpy(wl._normal_residual(rng, T, wl.N_STREAMS, wl.WIDTH)).cuda()
+        P = torch.from_numpy(wl._normal_residual(rng, T, wl.N_STREAMS, wl.WIDTH, 0.1)).cuda()
+        o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev))
+
+        def window_read(k, T=T, R=R, P=P, o=o):
+            ws = sets[k % N_SETS]
+            st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2],
+                                 stream.cuda_stream)
+            if st != 0:
+                raise binding.HCError(st, "hc_read")
+
+        for k in range(8):
+            window_read(k)
+        ms = time_region(stream, window_read, 96)
+        us_windows[str(T)] = round(ms * 1e3 / 96, 3)
+    print("# windows above 8 tokens, us per read: %s" % us_windows, file=sys.stderr, flush=True)
+
     ms_per_step = ms_eager / args.steps
     n_reads = args.steps * len(TS)
     weight_gbps = n_reads * WEIGHT_BYTES / (ms_eager * 1e-3) / 1e9
@@ -294,6 +321,7 @@ def main():
         "us_per_read": us_per_read,
         "graph": {"value": round(n_reads * WEIGHT_BYTES / (ms_graph * 1e-3) / 1e9, 2),
                   "ms_per_step": round(ms_graph / args.steps, 5), "us_per_read": us_graph},
+        "windows_us_per_read": us_windows,
         "prefill_T8192": prefill,
         "prefill": prefill_all,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,

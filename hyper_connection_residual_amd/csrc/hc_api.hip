@@ -151,10 +151,23 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
     if (st != HC_OK)
         return st;
 
-    if (T <= hc::kDecMaxT) {  // a short window: one launch
-        hipError_t e = hc::launch_decode(static_cast<int>(T), R, pending, w_norm, W_down, W_up,
-                                         out_mixed, out_bf16, out_fp16, ws->dec, hs);
-        return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
+    if (T <= hc::kDecSplitMaxT) {
+        // A short window: one launch per range of at most 8 consecutive tokens
+        // (ranges of near-equal size).  Every token's read is independent of
+        // the others, so the split changes no result.
+        const int n = static_cast<int>((T + hc::kDecMaxT - 1) / hc::kDecMaxT);
+        int t0 = 0;
+        for (int c = 0; c < n; ++c) {
+            const int left = static_cast<int>(T) - t0, chunks = n - c;
+            const int tc = (left + chunks - 1) / chunks;
+            const size_t in = static_cast<size_t>(t0) * hc::kD, out = static_cast<size_t>(t0) * hc::kWidth;
+            hipError_t e = hc::launch_decode(tc, R + in, pending ? pending + in : nullptr, w_norm, W_down, W_up,
+                                             out_mixed + out, out_bf16 + out, out_fp16 + out, ws->dec, hs);
+            if (e != hipSuccess)
+                return record(e, HC_ERR_LAUNCH);
+            t0 += tc;
+        }
+        return HC_OK;
     }
     st = wide_workspace(ws);
     if (st != HC_OK)

@@ -4,6 +4,8 @@ Every case prints what it runs before its GPU step.  Bars: the fp32 output
 within max|diff| / max|oracle| <= 2e-6, and the bf16 / fp16 images within
 1 ulp of the oracle's images on >= 99.9 % of the values (tests/hc_testlib.py).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -74,6 +76,31 @@ def test_ragged_token_counts(T):
     inp = wl.config_inputs(2, T=T, weight_set=1)
     gpu = hip_read(to_device(inp))
     assert_parity(gpu, _oracle(inp), label="T=%d" % T)
+
+
+@pytest.mark.parametrize("T, pending", [(16, True), (24, False), (32, True), (33, True)])
+def test_windows_above_eight(T, pending):
+    """9..32 tokens run as ceil(T / 8) short-window launches over consecutive
+    token ranges; 33 is the first count on the wide path.  Full oracle."""
+    _case("window of %d tokens, pending=%s" % (T, pending))
+    inp = wl.config_inputs(2, T=T, weight_set=5)
+    if not pending:
+        inp.pending = None
+    gpu = hip_read(to_device(inp))
+    assert_parity(gpu, _oracle(inp), label="T=%d pending=%s" % (T, pending))
+
+
+def test_split_window_equals_its_ranges():
+    """A 16-token window is two launches of 8: bitwise the reads of its halves."""
+    _case("T=16 against two T=8 reads of its halves")
+    inp = wl.config_inputs(2, T=16, weight_set=9)
+    whole = hip_read(to_device(inp))
+    for lo in (0, 8):
+        half = dataclasses.replace(inp, R=inp.R[lo:lo + 8].copy(), pending=inp.pending[lo:lo + 8].copy())
+        part = hip_read(to_device(half))
+        for a, b in zip(part, whole):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + 8])
 
 
 def test_outlier_channels_full_oracle():
