@@ -32,9 +32,10 @@ constexpr float kEps = 1e-6f;
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 8;
 // Up to this many tokens a read runs as ceil(T / 8) short-window launches over
-// consecutive token ranges; beyond it the wide path's fixed cost (~40 us) is
-// lower than re-streaming the weights once per 8 tokens (~9 us a launch).
-constexpr int kDecSplitMaxT = 32;
+// consecutive token ranges; beyond it the wide path (~30 us for 25..128
+// tokens) costs less than streaming the weights once per 8 tokens (~9 us a
+// launch).
+constexpr int kDecSplitMaxT = 24;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;

@@ -696,11 +696,38 @@ int tiles_of(int tokens)
     return (tokens + kTok - 1) / kTok;
 }
 
-// P1's split count: stream halves when that already gives a workgroup per
-// CU, else stream quarters.
+// P1's split count.  A workgroup takes a whole CU (its LDS), so the grid
+// should fill the chip once: chunks of 4096 tokens (32 tiles) use stream
+// halves, longer-than-1024-token chunks stream quarters (as before: 144-496
+// workgroups); shorter chunks split K finer so that short reads still stream
+// W_down over most of the chip: 32 splits (320 columns) for 4-8 tiles, 80
+// splits (128 columns, the narrowest the ring takes: 4 K steps) for 1-3
+// tiles.  The partial array never holds more than 16 x 3968 (split, token)
+// slots.
 int splits_for(int tokens)
 {
-    return (tokens + kDnTok - 1) / kDnTok * 8 >= 256 ? 8 : 16;
+    const int tiles = (tokens + kDnTok - 1) / kDnTok;
+    if (tiles * 8 >= 256)
+        return 8;
+    if (tiles > 8)
+        return 16;
+    if (tiles > 3)
+        return 32;
+    return 80;
+}
+
+template <int S>
+void launch_down_lo(int Tc, int tiles, const float* Rc, const float* Pc, const float* w_norm,
+                    const uint16_t* W_down, float* part, float* ssq, uint4* planes, hipStream_t stream)
+{
+    const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
+    if (Pc)
+        hipLaunchKernelGGL((prefill_down<S, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+    else
+        hipLaunchKernelGGL((prefill_down<S, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+    const int items = tiles * kTok * (kRank / 4);
+    hipLaunchKernelGGL(prefill_lo<S>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq,
+                       planes);
 }
 
 // (split, token) slots of the partial array, enough for any chunk of up to
@@ -738,29 +765,14 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         const size_t in_off = (size_t)c0 * kD, out_off = (size_t)c0 * kWidth;
         const float* Rc = R + in_off;
         const float* Pc = P ? P + in_off : nullptr;
-        const int S = splits_for(Tc);
-        const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
-        if (S == 8) {
-            if (Pc)
-                hipLaunchKernelGGL((prefill_down<8, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
-            else
-                hipLaunchKernelGGL((prefill_down<8, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
-        } else {
-            if (Pc)
-                hipLaunchKernelGGL((prefill_down<16, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
-            else
-                hipLaunchKernelGGL((prefill_down<16, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+        const int tiles = tiles_of(Tc);
+        switch (splits_for(Tc)) {
+        case 8: launch_down_lo<8>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
+        case 16: launch_down_lo<16>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
+        case 32: launch_down_lo<32>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
+        default: launch_down_lo<80>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
         }
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        const int tiles = tiles_of(Tc);
-        const int items = tiles * kTok * (kRank / 4);
-        if (S == 8)
-            hipLaunchKernelGGL(prefill_lo<8>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq, planes);
-        else
-            hipLaunchKernelGGL(prefill_lo<16>, dim3((items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq, planes);
-        e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         const int grid3 = 8 * kGroupsPerXcd * tiles;

@@ -89,8 +89,8 @@ extern "C" {
  *   stream     hipStream_t to run on (NULL = default stream)
  *
  * T <= 8 runs one launch of the short-window (verify-window) kernel; 9 <= T
- * <= 32 runs ceil(T / 8) of them, on consecutive ranges of at most 8 tokens
- * (a token's read does not depend on the other tokens, and below 33 tokens
+ * <= 24 runs ceil(T / 8) of them, on consecutive ranges of at most 8 tokens
+ * (a token's read does not depend on the other tokens, and up to 24 tokens
  * streaming the weights once per range costs less than the wide path's fixed
  * cost); larger T runs the wide (prefill) path.  Every valid T is handled;
  * there is no fallback to return.

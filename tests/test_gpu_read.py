@@ -78,10 +78,10 @@ def test_ragged_token_counts(T):
     assert_parity(gpu, _oracle(inp), label="T=%d" % T)
 
 
-@pytest.mark.parametrize("T, pending", [(16, True), (24, False), (32, True), (33, True)])
+@pytest.mark.parametrize("T, pending", [(16, True), (24, False), (25, True), (33, True)])
 def test_windows_above_eight(T, pending):
-    """9..32 tokens run as ceil(T / 8) short-window launches over consecutive
-    token ranges; 33 is the first count on the wide path.  Full oracle."""
+    """9..24 tokens run as ceil(T / 8) short-window launches over consecutive
+    token ranges; 25 is the first count on the wide path.  Full oracle."""
     _case("window of %d tokens, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=5)
     if not pending:
@@ -127,18 +127,19 @@ def test_full_size_configs_sampled(config):
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="config%d sampled" % config)
 
 
-@pytest.mark.parametrize("T, pending", [(128, False), (129, True), (3968, False), (3969, True), (4097, False),
-                                        (4097, True)])
+@pytest.mark.parametrize("T, pending", [(128, False), (129, True), (384, False), (385, True), (1024, True),
+                                        (1025, False), (3968, False), (3969, True), (4097, False), (4097, True)])
 def test_wide_path_boundaries(T, pending):
     """Token counts at the wide path's internal boundaries: one token past a
-    128-token down tile, the last count with stream-quarter splits (3968) and
-    the first with stream halves (3969), and one token past a 4096-token chunk
-    (the second chunk holds a single token).  Oracle on the tokens around each
-    boundary plus a random sample."""
+    128-token down tile; the down projection's K-split count changes from 80
+    (128-column splits) to 32 after 384 tokens, to 16 (stream quarters) after
+    1024 and to 8 (stream halves) after 3968; one token past a 4096-token
+    chunk (the second chunk holds a single token).  Oracle on the tokens
+    around each boundary plus a random sample."""
     _case("wide path boundary: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(5 if pending else 3, T=T, seed=T)
     gpu = hip_read(to_device(inp))
-    edges = {t for b in (64, 127, 128, 129, 3968, 4095, 4096) for t in (b - 1, b) if 0 <= t < T}
+    edges = {t for b in (64, 127, 128, 129, 384, 1024, 3968, 4095, 4096) for t in (b - 1, b) if 0 <= t < T}
     toks = np.array(sorted(set(_sample_tokens(T, k=24, seed=T).tolist()) | edges))
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="T=%d pending=%s" % (T, pending))
 
