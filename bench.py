@@ -11,9 +11,11 @@ on the next weight set).  Inputs are resident in HBM before timing starts.
 Prints ONE JSON line.  `value` = weight bytes streamed per second over the
 timed sweeps (GB/s), one hc_read call per read; the same sweeps replayed from
 captured HIP graphs (one graph per step) are reported under `graph`.  Per-T
-microseconds per read, the times of windows of 9..64 tokens and the prefill
-read times are reported beside it.  The roofline object describes the
-short-window kernel; the CPU baseline is the plain oracle on the host.
+microseconds per read, the times of windows of 9..64 tokens, the read with
+the pending write committed (hc_read_commit) against the read plus a separate
+R += pending, and the prefill read times are reported beside it.  The
+roofline object describes the short-window kernel; the CPU baseline is the
+plain oracle on the host.
 """
 from __future__ import annotations
 
@@ -199,6 +201,38 @@ def main():
         us_windows[str(T)] = round(ms * 1e3 / 96, 3)
     print("# windows above 8 tokens, us per read: %s" % us_windows, file=sys.stderr, flush=True)
 
+    # ---- the pending write committed by the read (hc_read_commit) against
+    # the read followed by a separate R += pending, at T = 8 and T = 8192
+    commit = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for T in (8, 8192):
+        R = torch.randn((T, 4, 2560), generator=gen, device=dev)
+        P = 0.1 * torch.randn((T, 4, 2560), generator=gen, device=dev)
+        o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev),
+             torch.empty((T, 2560), dtype=torch.int16, device=dev))
+
+        def call(fn, k, T=T, R=R, P=P, o=o):
+            ws = sets[k % N_SETS]
+            st = fn(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2], stream.cuda_stream)
+            if st != 0:
+                raise binding.HCError(st, "read")
+
+        def read_then_add(k, R=R, P=P):
+            call(binding.hc_read, k)
+            R.add_(P)
+
+        n = 96 if T <= 8 else 10
+        for k in range(4):
+            call(binding.hc_read_commit, k)
+            read_then_add(k)
+        ms_c = time_region(stream, lambda k: call(binding.hc_read_commit, k), n)
+        ms_a = time_region(stream, read_then_add, n)
+        commit[str(T)] = {"read_commit_us": round(ms_c * 1e3 / n, 3), "read_then_add_us": round(ms_a * 1e3 / n, 3)}
+        del R, P, o
+    print("# pending write committed: %s" % commit, file=sys.stderr, flush=True)
+
     ms_per_step = ms_eager / args.steps
     n_reads = args.steps * len(TS)
     weight_gbps = n_reads * WEIGHT_BYTES / (ms_eager * 1e-3) / 1e9
@@ -322,6 +356,7 @@ def main():
         "graph": {"value": round(n_reads * WEIGHT_BYTES / (ms_graph * 1e-3) / 1e9, 2),
                   "ms_per_step": round(ms_graph / args.steps, 5), "us_per_read": us_graph},
         "windows_us_per_read": us_windows,
+        "commit": commit,
         "prefill_T8192": prefill,
         "prefill": prefill_all,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,

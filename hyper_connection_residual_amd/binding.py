@@ -26,6 +26,7 @@ HC_ERR_LAUNCH = 5
 _P = ctypes.c_void_p
 SIGNATURES = {
     "hc_read": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hc_read_commit": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hc_last_hip_error": (ctypes.c_int, []),
     "hc_dims": (None, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
@@ -86,6 +87,15 @@ def hc_read(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, 
                              _stream(stream))
 
 
+def hc_read_commit(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, stream=None):
+    """hc_read_commit of the C ABI: hc_read, then R <- R + pending in place.
+
+    Returns the status code (0 = HC_OK)."""
+    return library().hc_read_commit(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
+                                    _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
+                                    _stream(stream))
+
+
 def hc_status_string(status: int) -> str:
     return library().hc_status_string(int(status)).decode()
 
@@ -125,10 +135,11 @@ def _check(t, name, dtype, shape):
         raise ValueError("%s must be contiguous" % name)
 
 
-def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None):
+def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None, commit=False):
     """The hyper-connection read on the current stream.
 
     R, pending: float32 [T, 4, 2560]; w_norm: float32 [4, 2560];
+    commit=True also writes R + pending back into R (hc_read_commit);
     W_down: bf16 bits as int16/uint16 [320, 10240] (or a torch.bfloat16 tensor);
     W_up: [10240, 320] likewise.  Returns (mixed float32 [T, 2560],
     bf16 image as torch.bfloat16 [T, 2560], fp16 image as torch.float16 [T, 2560]).
@@ -155,7 +166,8 @@ def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None):
     _check(mixed, "out_mixed", torch.float32, (T, C))
     _check(img_bf16, "out_bf16", img_bf16.dtype, (T, C))
     _check(img_fp16, "out_fp16", img_fp16.dtype, (T, C))
-    st = hc_read(T, R, pending, w_norm, W_down, W_up, mixed, img_bf16, img_fp16, stream)
+    fn = hc_read_commit if commit else hc_read
+    st = fn(T, R, pending, w_norm, W_down, W_up, mixed, img_bf16, img_fp16, stream)
     if st != HC_OK:
-        raise HCError(st, "hc_read")
+        raise HCError(st, fn.__name__)
     return mixed, img_bf16, img_fp16

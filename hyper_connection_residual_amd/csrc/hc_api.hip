@@ -127,13 +127,10 @@ int wide_workspace(Workspace* ws)
     return HC_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-HC_API int hc_read(int64_t T, const float* R, const float* pending, const float* w_norm,
-                   const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                   uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
+// The read of hc_read and hc_read_commit; R_commit is NULL or R.
+int read_impl(int64_t T, const float* R, const float* pending, const float* w_norm, const uint16_t* W_down,
+              const uint16_t* W_up, float* out_mixed, uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
+              void* stream)
 {
     if (T < 1 || !R || !w_norm || !W_down || !W_up || !out_mixed || !out_bf16 || !out_fp16)
         return HC_ERR_ARG;
@@ -141,6 +138,8 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
         !aligned16(W_down) || !aligned16(W_up) || !aligned16(out_mixed) ||
         !aligned16(out_bf16) || !aligned16(out_fp16))
         return HC_ERR_ALIGN;
+    if (!pending)
+        R_commit = nullptr;  // nothing to commit
     int dev = 0;
     int st = current_device(&dev);
     if (st != HC_OK)
@@ -162,7 +161,8 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
             const int tc = (left + chunks - 1) / chunks;
             const size_t in = static_cast<size_t>(t0) * hc::kD, out = static_cast<size_t>(t0) * hc::kWidth;
             hipError_t e = hc::launch_decode(tc, R + in, pending ? pending + in : nullptr, w_norm, W_down, W_up,
-                                             out_mixed + out, out_bf16 + out, out_fp16 + out, ws->dec, hs);
+                                             out_mixed + out, out_bf16 + out, out_fp16 + out,
+                                             R_commit ? R_commit + in : nullptr, ws->dec, hs);
             if (e != hipSuccess)
                 return record(e, HC_ERR_LAUNCH);
             t0 += tc;
@@ -172,9 +172,27 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
     st = wide_workspace(ws);
     if (st != HC_OK)
         return st;
-    hipError_t e = hc::launch_prefill(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16,
-                                      out_fp16, ws->wide_base, hc::kPrefillChunk, hs);
+    hipError_t e = hc::launch_prefill(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R_commit,
+                                      ws->wide_base, hc::kPrefillChunk, hs);
     return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
+}
+
+}  // namespace
+
+extern "C" {
+
+HC_API int hc_read(int64_t T, const float* R, const float* pending, const float* w_norm,
+                   const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                   uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
+{
+    return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, nullptr, stream);
+}
+
+HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float* w_norm,
+                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                          uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
+{
+    return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R, stream);
 }
 
 HC_API const char* hc_status_string(int status)

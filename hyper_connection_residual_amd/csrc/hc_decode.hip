@@ -341,9 +341,10 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint4* lds_wave_base)
 // them from memory (a fetch that queues behind the other CUs' weight traffic).
 template <int T>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
-    const uint16_t* __restrict__ W_down, const uint16_t* __restrict__ W_up, const float* __restrict__ R,
+    const uint16_t* __restrict__ W_down, const uint16_t* __restrict__ W_up, const float* R,
     const float* __restrict__ P, const float* __restrict__ w_norm, uint64_t* __restrict__ scratch,
-    float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16)
+    float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16,
+    float* R_commit)
 {
     static_assert(T >= 1 && T <= kDecMaxT, "short-window kernel takes 1..8 tokens");
     static_assert(kDecRowsPerXcd * kRowChunks == kTileChunks && kUpRows * kRowChunks == kTileChunks,
@@ -758,10 +759,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         HC_PROBE(7, wave == 0 && lane == 0);
     }
     wait_all_loads();  // the W_up tile and R' have landed
+    const float rprime = P ? mr + mp : mr;
     if (threadIdx.x < kUpRows * T)
-        rpl[threadIdx.x] = P ? mr + mp : mr;  // it = 40 t + row
+        rpl[threadIdx.x] = rprime;  // it = 40 t + row
     wg_barrier();  // B2: lo and R' staged, W_up tile complete
     HC_PROBE(8, threadIdx.x == 0);
+    // (10') the pending write committed: R' of this workgroup's 40 (stream,
+    //      column) pairs back into R.  No read of these elements is left
+    //      anywhere: every workgroup read them for its down part before it
+    //      stored the partials that hop 2 has just waited for, and no other
+    //      workgroup mixes these columns.
+    if (R_commit && P && threadIdx.x < kUpRows * T) {
+        const int at = threadIdx.x / kUpRows, row = threadIdx.x - at * kUpRows;
+        R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime;
+    }
 
     if (wave < 3) {
         // (11) up projection: wave w < 3 takes tile rows 16 w .. +15 (slot n =
@@ -842,11 +853,11 @@ hipError_t decode_resident_blocks(int* blocks_per_cu)
 
 hipError_t launch_decode(int T, const float* R, const float* P, const float* w_norm,
                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                         uint16_t* out_bf16, uint16_t* out_fp16, const DecodeScratch& s,
-                         hipStream_t stream)
+                         uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
+                         const DecodeScratch& s, hipStream_t stream)
 {
     uint64_t* scratch = s.part;  // the carve's base: the kernel derives the rest
-    void* args[] = {&W_down, &W_up, &R, &P, &w_norm, &scratch, &out_mixed, &out_bf16, &out_fp16};
+    void* args[] = {&W_down, &W_up, &R, &P, &w_norm, &scratch, &out_mixed, &out_bf16, &out_fp16, &R_commit};
     const void* fn = nullptr;
     switch (T) {
     case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;

@@ -60,10 +60,11 @@ void decode_scratch_carve(void* base, DecodeScratch* s);
 // Workgroups of the short-window kernel that fit on one CU at once.
 hipError_t decode_resident_blocks(int* blocks_per_cu);
 
+// R_commit: NULL, or R itself, which then receives R' = R + P (with P given).
 hipError_t launch_decode(int T, const float* R, const float* P, const float* w_norm,
                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                         uint16_t* out_bf16, uint16_t* out_fp16, const DecodeScratch& s,
-                         hipStream_t stream);
+                         uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
+                         const DecodeScratch& s, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Wide path (T > kDecMaxT): three launches per chunk of up to kPrefillChunk
@@ -75,7 +76,7 @@ size_t prefill_scratch_bytes(int chunk);
 
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                          uint16_t* out_bf16, uint16_t* out_fp16, void* scratch, int chunk,
-                          hipStream_t stream);
+                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, void* scratch,
+                          int chunk, hipStream_t stream);
 
 }  // namespace hc

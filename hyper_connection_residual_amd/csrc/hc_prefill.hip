@@ -471,11 +471,12 @@ constexpr int kUpLoads = (kUpWChunks + kLoTile) / 64 / 4;  // wave instructions 
 template <bool HAS_P>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
-                                                        const float* __restrict__ R,
+                                                        const float* R,
                                                         const float* __restrict__ P,
                                                         float* __restrict__ out_mixed,
                                                         uint16_t* __restrict__ out_bf16,
-                                                        uint16_t* __restrict__ out_fp16)
+                                                        uint16_t* __restrict__ out_fp16,
+                                                        float* R_commit)
 {
     __shared__ __align__(16) uint4 lds[kUpSlots * kUpStage];
 
@@ -642,6 +643,17 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                 rv[cb][s].z += pv.z;
                 rv[cb][s].w += pv.w;
             }
+        // the pending write committed: R' of this lane's token and columns
+        // back into R (no other workgroup reads them in this chunk, and the
+        // down projection of the chunk has finished)
+        if (R_commit && t < T) {
+            float* crow = R_commit + (size_t)t * kD + c0 + 4 * g;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    *reinterpret_cast<float4*>(crow + s * kWidth + 16 * cb) = rv[cb][s];
+        }
     }
     // The wave's 16 tokens x 64 columns of mixed go through 4 KB of LDS of its
     // own (inside ring slot 1, which the last step does not read) so that
@@ -752,8 +764,8 @@ size_t prefill_scratch_bytes(int chunk)
 
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                          uint16_t* out_bf16, uint16_t* out_fp16, void* scratch, int chunk,
-                          hipStream_t stream)
+                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, void* scratch,
+                          int chunk, hipStream_t stream)
 {
     const size_t slots = part_slots(chunk);
     float* part = static_cast<float*>(scratch);  // [S][Tc][320]
@@ -776,12 +788,13 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         if (e != hipSuccess)
             return e;
         const int grid3 = 8 * kGroupsPerXcd * tiles;
+        float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
         if (Pc)
             hipLaunchKernelGGL(prefill_upmix<true>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
-                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off);
+                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
         else
             hipLaunchKernelGGL(prefill_upmix<false>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
-                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off);
+                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;

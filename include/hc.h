@@ -100,6 +100,27 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
             const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
             uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
 
+/*
+ * hc_read_commit -- hc_read, and the pending write committed: R[t][s][c]
+ * becomes R'[t][s][c] = fl32(R + pending), the pending-updated residual the
+ * read itself applies first ("#2488 sycl/A770: faster hyper-connection read",
+ * Summary item 4; "#315 hc: the multi-token hyper-connection read split
+ * finer", Exactness: reads with and without the pending write).  The pages
+ * only apply the pending write inside the read; writing it back is this
+ * library's extension, so that the engine needs no separate residual update.
+ *
+ * Arguments as for hc_read, except that R is read and then overwritten in
+ * place (caller-owned, [T][4][2560] fp32).  The outputs are the ones hc_read
+ * gives for the same inputs, bit for bit.  With pending == NULL there is
+ * nothing to commit and R is left untouched.  R must not overlap pending,
+ * w_norm, the weights or the outputs.  If the call returns an error, R may
+ * hold a mix of old and committed values.
+ * Returns HC_OK or an HC_ERR_* code.
+ */
+HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float* w_norm,
+                   const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                   uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
+
 /* Text for a status code (static storage; never NULL). */
 HC_API const char* hc_status_string(int status);
 

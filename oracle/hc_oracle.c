@@ -413,3 +413,28 @@ int hc_oracle_read(int64_t T, int n, int C, int r, double eps,
     free(wu);
     return status;
 }
+
+/*
+ * The pending write committed: R'[i] = fl32(R[i] + P[i]) for `count`
+ * elements, the same R' the read above starts from ("#2488 sycl/A770: faster
+ * hyper-connection read", Summary item 4: the pending-updated residual; "#315
+ * hc: the multi-token hyper-connection read split finer", Exactness: reads
+ * with and without the pending write).  Writing it back into R is an
+ * extension of the library, not a step of the pages; this is its reference.
+ * P == NULL copies R (nothing to commit).  out may be R itself.
+ * Returns 0, or 1 on a bad argument.
+ */
+int hc_oracle_commit(int64_t count, const float* R, const float* P, float* out)
+{
+    if (count < 0 || !R || !out)
+        return HC_ORACLE_EARG;
+    for (int64_t i = 0; i < count; ++i) {
+        float v = R[i];
+        if (P) {
+            float sum = R[i] + P[i];
+            v = sum;
+        }
+        out[i] = v;
+    }
+    return HC_ORACLE_OK;
+}

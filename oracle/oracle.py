@@ -52,6 +52,8 @@ def load():
     lib.hc_oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.hc_oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.hc_oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.hc_oracle_commit.argtypes = [ctypes.c_int64, p, p, p]
+    lib.hc_oracle_commit.restype = ctypes.c_int
     lib.hc_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.hc_oracle_bf16_to_double.restype = ctypes.c_double
     _lib = lib
@@ -107,6 +109,22 @@ def oracle_read(R, w_norm, W_down, W_up, pending=None, *, eps=1e-6,
     if want_lo:
         out.append(lo)
     return out[0] if len(out) == 1 else tuple(out)
+
+
+def oracle_commit(R, pending):
+    """R' = fl32(R + pending) elementwise (R unchanged when pending is None):
+    what hc_read_commit leaves in R.  float32 in, float32 out."""
+    lib = load()
+    R = _c(R, np.float32)
+    if pending is not None:
+        pending = _c(pending, np.float32)
+        if pending.shape != R.shape:
+            raise ValueError("pending must match R")
+    out = np.empty_like(R)
+    st = lib.hc_oracle_commit(R.size, _ptr(R), _ptr(pending), _ptr(out))
+    if st != 0:
+        raise RuntimeError("hc_oracle_commit failed with status %d" % st)
+    return out
 
 
 def oracle_images(mixed):

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == ["hc_read", "hc_status_string", "hc_last_hip_error", "hc_dims",
+    assert names == ["hc_read", "hc_read_commit", "hc_status_string", "hc_last_hip_error", "hc_dims",
                      "hc_timeouts", "hc_release"]
 
 
@@ -63,23 +63,25 @@ def test_status_strings(lib):
     assert binding.hc_status_string(99) == "unknown status"
 
 
-def test_argument_checks_happen_before_any_hip_call(lib):
+@pytest.mark.parametrize("entry", ["hc_read", "hc_read_commit"])
+def test_argument_checks_happen_before_any_hip_call(lib, entry):
     from hyper_connection_residual_amd import binding
+    fn = getattr(binding, entry)
     good = 0x10000  # never dereferenced: the checks below reject first
     args = [good] * 8
     # T < 1
-    assert binding.hc_read(0, *args, 0) == binding.HC_ERR_ARG
-    assert binding.hc_read(-5, *args, 0) == binding.HC_ERR_ARG
+    assert fn(0, *args, 0) == binding.HC_ERR_ARG
+    assert fn(-5, *args, 0) == binding.HC_ERR_ARG
     # a required pointer is NULL (pending may be NULL)
     for i in (0, 2, 3, 4, 5, 6, 7):
         a = list(args)
         a[i] = None
-        assert binding.hc_read(1, *a, 0) == binding.HC_ERR_ARG, i
+        assert fn(1, *a, 0) == binding.HC_ERR_ARG, i
     # misalignment of any pointer, pending included
     for i in range(8):
         a = list(args)
         a[i] = good + 4
-        assert binding.hc_read(1, *a, 0) == binding.HC_ERR_ALIGN, i
+        assert fn(1, *a, 0) == binding.HC_ERR_ALIGN, i
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
@@ -87,8 +89,9 @@ def test_argument_checks_happen_before_any_hip_call(lib):
 def test_no_device_is_an_error_not_a_fallback(lib):
     from hyper_connection_residual_amd import binding
     good = 0x10000
-    st = binding.hc_read(1, good, None, good, good, good, good, good, good, 0)
-    assert st == binding.HC_ERR_DEVICE
+    for fn in (binding.hc_read, binding.hc_read_commit):
+        st = fn(1, good, good, good, good, good, good, good, good, 0)
+        assert st == binding.HC_ERR_DEVICE
 
 
 def test_python_read_refuses_cpu_tensors(lib):

@@ -103,6 +103,27 @@ def test_split_window_equals_its_ranges():
                                   (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + 8])
 
 
+@pytest.mark.parametrize("T, pending", [(1, True), (5, True), (8, False), (16, True), (300, True), (4097, True)])
+def test_commit_writes_the_pending_update(T, pending):
+    """hc_read_commit: the outputs are hc_read's, bit for bit, and R then holds
+    the oracle's committed residual fl32(R + pending), bit for bit (untouched
+    without a pending write).  Covers the short-window kernel, the split
+    window, and the wide path over two chunks."""
+    _case("commit: T=%d, pending=%s" % (T, pending))
+    inp = wl.config_inputs(2, T=T, weight_set=2) if T <= 24 else wl.config_inputs(5, T=T, seed=T)
+    if not pending:
+        inp.pending = None
+    dev = to_device(inp)
+    plain = hip_read(dev)
+    committed = hip_read(dev, commit=True)
+    for a, b in zip(committed, plain):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+    want = orc.oracle_commit(inp.R, inp.pending)
+    got = dev["R"].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 def test_outlier_channels_full_oracle():
     _case("config 3 distributions at T=300 (several tiles, ragged tail), full oracle")
     inp = wl.config_inputs(3, T=300)

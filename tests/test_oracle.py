@@ -285,6 +285,39 @@ def test_pending_equals_preadded_residual(small_case):
                           orc.oracle_read(i.R, i.w_norm, i.W_down, i.W_up, None))
 
 
+def test_commit_hand_values():
+    """The committed residual is the IEEE binary32 sum, rounded to nearest even:
+    ties go to the even neighbour, x + (-x) is +0, -0 + -0 is -0, overflow
+    goes to infinity, subnormals add exactly."""
+    f = np.float32
+    R = np.array([1, 1, 1, 3, -0.0, 3.4028235e38, 1e-45, 2.5], dtype=f)
+    P = np.array([2.0 ** -24, 3 * 2.0 ** -24, -2.0 ** -25, -3, -0.0, 3.4028235e38, 1e-45, 0.0], dtype=f)
+    out = orc.oracle_commit(R, P)
+    want = np.array([1, 1 + 2.0 ** -22, 1, 0, -0.0, np.inf, 2.8e-45, 2.5], dtype=f)
+    assert np.array_equal(out.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(orc.oracle_commit(R, None), R)
+
+
+def test_commit_matches_exact_sum_rounded_once():
+    """For N(0,1) + N(0,0.1) operands the sum is exact in binary64 (exponents
+    differ by far less than 29), so one binary64 -> binary32 rounding gives
+    the correctly rounded float sum."""
+    rng = np.random.default_rng(5)
+    R = rng.standard_normal(100000).astype(np.float32)
+    P = (0.1 * rng.standard_normal(100000)).astype(np.float32)
+    want = (R.astype(np.float64) + P.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(orc.oracle_commit(R, P).view(np.uint32), want.view(np.uint32))
+
+
+def test_commit_is_the_reads_own_residual(small_case):
+    """Reading the committed residual without a pending write gives the read
+    with the pending write, bit for bit."""
+    i = small_case
+    m = orc.oracle_read(i.R, i.w_norm, i.W_down, i.W_up, i.pending)
+    Rc = orc.oracle_commit(i.R, i.pending)
+    assert np.array_equal(m, orc.oracle_read(Rc, i.w_norm, i.W_down, i.W_up, None))
+
+
 def test_tokens_are_independent(small_case):
     i = small_case
     m = orc.oracle_read(i.R, i.w_norm, i.W_down, i.W_up, i.pending)
