@@ -1,12 +1,16 @@
 // hc_api.hip -- host side of the C ABI declared in include/hc.h: argument
-// checks, per-(device, stream) scratch workspaces, and dispatch to the
-// short-window (T <= 8) and wide (prefill) kernels.
+// checks, per-(device, stream) scratch workspaces, the start-up check of the
+// short-window kernel, and dispatch to the short-window (T <= 24, in launches
+// of up to 8 tokens) and wide (prefill) kernels.
 #include "hc.h"
 #include "hc_internal.h"
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -29,6 +33,10 @@ struct Workspace {
 std::mutex g_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace*> g_workspaces;
 std::map<int, bool> g_device_ok;
+// Result of the start-up check of the short-window kernel per device (absent:
+// not run yet).  Guarded by g_check_mutex, which is taken before g_mutex.
+std::mutex g_check_mutex;
+std::map<int, bool> g_short_window;
 
 int record(hipError_t e, int status)
 {
@@ -54,15 +62,7 @@ int current_device(int* dev)
         e = hipGetDeviceProperties(&prop, *dev);
         if (e != hipSuccess)
             return record(e, HC_ERR_DEVICE);
-        bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        if (ok) {
-            // every workgroup of the short-window kernel must be resident at once
-            int per_cu = 0;
-            e = hc::decode_resident_blocks(&per_cu);
-            if (e != hipSuccess)
-                return record(e, HC_ERR_DEVICE);
-            ok = per_cu * prop.multiProcessorCount >= hc::kDecWGs;
-        }
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         it = g_device_ok.emplace(*dev, ok).first;
     }
     return it->second ? HC_OK : record(hipSuccess, HC_ERR_DEVICE);
@@ -127,6 +127,143 @@ int wide_workspace(Workspace* ws)
     return HC_OK;
 }
 
+bool log_enabled()
+{
+    const char* v = std::getenv("HC_LOG");
+    return !(v && v[0] == '0' && v[1] == 0);
+}
+
+// Deterministic check inputs: values uniform in [-a, a) from a 32-bit
+// xorshift, and bf16 bit patterns of such values (round to nearest even).
+struct CheckRng {
+    uint32_t x = 2463534242u;
+    float next(float a)
+    {
+        x ^= x << 13;
+        x ^= x >> 17;
+        x ^= x << 5;
+        return a * (2.0f * (float)(x >> 8) * (1.0f / 16777216.0f) - 1.0f);
+    }
+    uint16_t bf16(float a)
+    {
+        const float f = next(a);
+        uint32_t u;
+        std::memcpy(&u, &f, 4);
+        return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+};
+
+// The start-up check of the short-window kernel on one device (the pages'
+// kernels check themselves once per card and fall back to the plain kernel
+// on any disagreement: "#315 hc: the multi-token hyper-connection read split
+// finer", Exactness).  Its hand-offs need all 256 workgroups resident at once
+// and the dispatcher's placement of workgroups on XCDs; the check reads 8
+// tokens with pending once through it and once through the wide path (which
+// needs neither) and keeps it only if (a) every workgroup fits, (b) no
+// bounded wait expired and (c) the two outputs agree to 4e-6 of their largest
+// value (each is within 2e-6 of the exact read).  Otherwise windows of up to
+// 24 tokens take the wide path.  The bounded waits' limit can be lowered with
+// HC_SELFCHECK_WAIT_TICKS (ticks of the 100 MHz clock) to force the
+// fallback.  One line per device goes to stderr (HC_LOG=0 silences it).
+int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t why_len)
+{
+    *on = false;
+    int per_cu = 0;
+    hipError_t e = hc::decode_resident_blocks(&per_cu);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_DEVICE);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_DEVICE);
+    if (per_cu * cus < hc::kDecWGs) {
+        std::snprintf(why, why_len, "%d workgroups per CU x %d CUs cannot hold %d", per_cu, cus, hc::kDecWGs);
+        return HC_OK;
+    }
+    int st = wide_workspace(ws);
+    if (st != HC_OK)
+        return st;
+    constexpr int T = hc::kDecMaxT;
+    const size_t nin = (size_t)T * hc::kD, nw = (size_t)hc::kRank * hc::kD, nout = (size_t)T * hc::kWidth;
+    CheckRng rng;
+    std::vector<float> R(nin), P(nin), w(hc::kD);
+    std::vector<uint16_t> Wd(nw), Wu(nw);
+    for (auto& v : R) v = rng.next(1.7f);
+    for (auto& v : P) v = rng.next(0.17f);
+    for (auto& v : w) v = 1.0f + rng.next(0.17f);
+    for (auto& v : Wd) v = rng.bf16(0.035f);
+    for (auto& v : Wu) v = rng.bf16(0.035f);
+    const size_t bytes = 4 * (2 * nin + hc::kD) + 2 * (2 * nw) + 2 * (4 * nout + 4 * nout);
+    char* buf = nullptr;
+    e = hipMalloc(&buf, bytes);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_NOMEM);
+    float* dR = reinterpret_cast<float*>(buf);
+    float* dP = dR + nin;
+    float* dw = dP + nin;
+    uint16_t* dWd = reinterpret_cast<uint16_t*>(dw + hc::kD);
+    uint16_t* dWu = dWd + nw;
+    float* m1 = reinterpret_cast<float*>(dWu + nw);
+    float* m2 = m1 + nout;
+    uint16_t* img = reinterpret_cast<uint16_t*>(m2 + nout);  // 4 images of nout
+    uint32_t expired = 0;
+    std::vector<float> a(nout), b(nout);
+    const char* env = std::getenv("HC_SELFCHECK_WAIT_TICKS");
+    const long long ticks = env ? std::atoll(env) : hc::kDecWaitTicks;
+    hipStream_t hs = ws->stream;
+    e = hipMemcpyAsync(dR, R.data(), 4 * nin, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dP, P.data(), 4 * nin, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dw, w.data(), 4 * hc::kD, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dWd, Wd.data(), 2 * nw, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(dWu, Wu.data(), 2 * nw, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
+    if (e == hipSuccess)
+        e = hc::launch_decode(T, dR, dP, dw, dWd, dWu, m1, img, img + nout, nullptr, ws->dec, hs, ticks);
+    if (e == hipSuccess)
+        e = hc::launch_prefill(T, dR, dP, dw, dWd, dWu, m2, img + 2 * nout, img + 3 * nout, nullptr, ws->wide_base,
+                               hc::kPrefillChunk, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(&expired, ws->dec.timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(a.data(), m1, 4 * nout, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(b.data(), m2, 4 * nout, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    const hipError_t ef = hipFree(buf);
+    if (e != hipSuccess || ef != hipSuccess)
+        return record(e != hipSuccess ? e : ef, HC_ERR_DEVICE);
+    double dmax = 0.0, vmax = 0.0;
+    bool finite = true;
+    for (size_t i = 0; i < nout; ++i) {
+        finite = finite && std::isfinite(a[i]) && std::isfinite(b[i]);
+        dmax = std::fmax(dmax, std::fabs((double)a[i] - (double)b[i]));
+        vmax = std::fmax(vmax, std::fabs((double)b[i]));
+    }
+    const double rel = vmax > 0.0 ? dmax / vmax : dmax;
+    *on = expired == 0 && finite && rel <= 4e-6;
+    std::snprintf(why, why_len, "%u expired waits, agrees with the wide path to %.1e", expired, rel);
+    return HC_OK;
+}
+
+// Whether windows of up to 24 tokens use the short-window kernel on `dev`;
+// the check runs on the first call for the device.
+int short_window_on(int dev, Workspace* ws, bool* on)
+{
+    std::lock_guard<std::mutex> lock(g_check_mutex);
+    auto it = g_short_window.find(dev);
+    if (it != g_short_window.end()) {
+        *on = it->second;
+        return HC_OK;
+    }
+    char why[160] = "";
+    const int st = run_short_window_check(dev, ws, on, why, sizeof why);
+    if (st != HC_OK)
+        return st;
+    g_short_window.emplace(dev, *on);
+    if (log_enabled())
+        std::fprintf(stderr, "hc: device %d: the short-window read is %s (start-up check: %s)%s\n", dev,
+                     *on ? "on" : "OFF", why, *on ? "" : "; windows of up to 24 tokens take the wide path");
+    return HC_OK;
+}
+
 // The read of hc_read and hc_read_commit; R_commit is NULL or R.
 int read_impl(int64_t T, const float* R, const float* pending, const float* w_norm, const uint16_t* W_down,
               const uint16_t* W_up, float* out_mixed, uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
@@ -149,8 +286,12 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
     st = workspace(dev, hs, &ws);
     if (st != HC_OK)
         return st;
+    bool short_ok = false;
+    st = short_window_on(dev, ws, &short_ok);
+    if (st != HC_OK)
+        return st;
 
-    if (T <= hc::kDecSplitMaxT) {
+    if (T <= hc::kDecSplitMaxT && short_ok) {
         // A short window: one launch per range of at most 8 consecutive tokens
         // (ranges of near-equal size).  Every token's read is independent of
         // the others, so the split changes no result.
@@ -193,6 +334,27 @@ HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float
                           uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
 {
     return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R, stream);
+}
+
+HC_API int hc_short_window_on(int* on)
+{
+    if (!on)
+        return HC_ERR_ARG;
+    *on = 0;
+    int dev = 0;
+    int st = current_device(&dev);
+    if (st != HC_OK)
+        return st;
+    Workspace* ws = nullptr;
+    st = workspace(dev, nullptr, &ws);
+    if (st != HC_OK)
+        return st;
+    bool b = false;
+    st = short_window_on(dev, ws, &b);
+    if (st != HC_OK)
+        return st;
+    *on = b ? 1 : 0;
+    return HC_OK;
 }
 
 HC_API const char* hc_status_string(int status)

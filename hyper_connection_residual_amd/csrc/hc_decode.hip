@@ -74,7 +74,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr long long kWaitTicks = 5000000;  // 50 ms of the 100 MHz wall clock
 constexpr int kTileChunks = 1600;           // 16-byte chunks in either weight tile (25,600 bytes)
 constexpr int kTileInstr = kTileChunks / 64;  // wave instructions per tile (25)
 constexpr int kRowChunks = kRank / 8;       // chunks per row of either tile (40: 320 bf16)
@@ -253,51 +252,6 @@ __device__ __forceinline__ void note_timeout(uint32_t* timeouts)
     __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Reads the T consecutive words at base1 + idx1 and at base2 + idx2 (both
-// even) into v1 and v2, polling until every tag carries `gen`.  Each polling
-// round issues all its loads before it looks at any of them, so a round costs
-// one memory latency whatever T is.  Returns false after a timeout (counted
-// once; the values read so far are then meaningless).
-template <int T>
-__device__ __forceinline__ bool poll_words(const uint64_t* base1, int idx1, const uint64_t* base2, int idx2,
-                                           uint32_t gen, long long t0, int lane, float (&v1)[T], float (&v2)[T],
-                                           uint32_t* timeouts, int site)
-{
-    constexpr int NP = (T + 1) / 2;
-    [[maybe_unused]] int rounds = 0;
-    while (true) {
-        ++rounds;
-        new_round();
-        uint4 a[NP], c[NP];
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            a[q] = ld_words2(base1, idx1 + 2 * q);
-            c[q] = ld_words2(base2, idx2 + 2 * q);
-        }
-        bool ok = true;
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            ok = ok && a[q].y == gen && c[q].y == gen && (2 * q + 1 >= T || (a[q].w == gen && c[q].w == gen));
-            v1[2 * q] = __uint_as_float(a[q].x);
-            v2[2 * q] = __uint_as_float(c[q].x);
-            if (2 * q + 1 < T) {
-                v1[2 * q + 1] = __uint_as_float(a[q].z);
-                v2[2 * q + 1] = __uint_as_float(c[q].z);
-            }
-        }
-        if (__all(ok)) {
-            HC_COUNT(site, 0, rounds, lane == 0);
-            return true;
-        }
-        if (wall_clock64() - t0 > kWaitTicks) {
-            if (lane == 0)
-                note_timeout(timeouts);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // ---- weight tiles in LDS.  A tile row holds RC chunks of 16 bytes (RC / 8
 // whole 128-byte lines).  The 8 chunks of a line are stored XOR-swizzled by
 // row, and in 80-chunk rows (whose pitch is a multiple of 256 bytes) odd rows
@@ -344,7 +298,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint16_t* __restrict__ W_down, const uint16_t* __restrict__ W_up, const float* R,
     const float* __restrict__ P, const float* __restrict__ w_norm, uint64_t* __restrict__ scratch,
     float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16,
-    float* R_commit)
+    float* R_commit, long long wait_ticks)
 {
     static_assert(T >= 1 && T <= kDecMaxT, "short-window kernel takes 1..8 tokens");
     static_assert(kDecRowsPerXcd * kRowChunks == kTileChunks && kUpRows * kRowChunks == kTileChunks,
@@ -608,7 +562,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     HC_COUNT(0, 0, rounds, lane == 0);
                     break;
                 }
-                if (wall_clock64() - t0 > kWaitTicks) {
+                if (wall_clock64() - t0 > wait_ticks) {
                     if (lane == 0)
                         note_timeout(s.timeouts);
                     break;
@@ -662,7 +616,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     HC_COUNT(0, 0, rounds, lane == 0);
                     break;
                 }
-                if (wall_clock64() - t0 > kWaitTicks) {
+                if (wall_clock64() - t0 > wait_ticks) {
                     if (lane == 0)
                         note_timeout(s.timeouts);
                     break;
@@ -727,7 +681,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 HC_COUNT(2, 1, rounds, wave == 0 && lane == 0);
                 break;
             }
-            if (wall_clock64() - t0 > kWaitTicks) {
+            if (wall_clock64() - t0 > wait_ticks) {
                 if (lane == 0)
                     note_timeout(s.timeouts);
                 break;
@@ -854,10 +808,11 @@ hipError_t decode_resident_blocks(int* blocks_per_cu)
 hipError_t launch_decode(int T, const float* R, const float* P, const float* w_norm,
                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
-                         const DecodeScratch& s, hipStream_t stream)
+                         const DecodeScratch& s, hipStream_t stream, long long wait_ticks)
 {
     uint64_t* scratch = s.part;  // the carve's base: the kernel derives the rest
-    void* args[] = {&W_down, &W_up, &R, &P, &w_norm, &scratch, &out_mixed, &out_bf16, &out_fp16, &R_commit};
+    void* args[] = {&W_down, &W_up, &R, &P, &w_norm, &scratch, &out_mixed, &out_bf16, &out_fp16, &R_commit,
+                    &wait_ticks};
     const void* fn = nullptr;
     switch (T) {
     case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;

@@ -60,11 +60,17 @@ void decode_scratch_carve(void* base, DecodeScratch* s);
 // Workgroups of the short-window kernel that fit on one CU at once.
 hipError_t decode_resident_blocks(int* blocks_per_cu);
 
+// Every bounded wait of the short-window kernel gives up after this many ticks
+// of the 100 MHz wall clock (50 ms), counts one expired wait and goes on.
+constexpr long long kDecWaitTicks = 5000000;
+
 // R_commit: NULL, or R itself, which then receives R' = R + P (with P given).
+// wait_ticks: the bounded waits' limit (kDecWaitTicks; the start-up check may
+// pass a smaller one).
 hipError_t launch_decode(int T, const float* R, const float* P, const float* w_norm,
                          const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
-                         const DecodeScratch& s, hipStream_t stream);
+                         const DecodeScratch& s, hipStream_t stream, long long wait_ticks = kDecWaitTicks);
 
 // ---------------------------------------------------------------------------
 // Wide path (T > kDecMaxT): three launches per chunk of up to kPrefillChunk

@@ -92,8 +92,13 @@ extern "C" {
  * <= 24 runs ceil(T / 8) of them, on consecutive ranges of at most 8 tokens
  * (a token's read does not depend on the other tokens, and up to 24 tokens
  * streaming the weights once per range costs less than the wide path's fixed
- * cost); larger T runs the wide (prefill) path.  Every valid T is handled;
- * there is no fallback to return.
+ * cost); larger T runs the wide (prefill) path.  The short-window kernel is
+ * used only where its start-up check passed (see hc_short_window_on);
+ * elsewhere every T runs the wide path.  Every valid T is handled; there is no
+ * fallback to return.
+ * The first call on a device runs that check (a few milliseconds, with
+ * synchronisation), and the first call on each stream allocates its
+ * workspace: neither may be under graph capture.
  * Returns HC_OK or an HC_ERR_* code.
  */
 HC_API int hc_read(int64_t T, const float* R, const float* pending, const float* w_norm,
@@ -120,6 +125,24 @@ HC_API int hc_read(int64_t T, const float* R, const float* pending, const float*
 HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float* w_norm,
                    const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
                    uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
+
+/*
+ * hc_short_window_on -- *on = 1 if the current device reads windows of up to
+ * 24 tokens with the short-window kernel, 0 if they take the wide path.  The
+ * kernel's hand-offs need its 256 workgroups resident together and placed on
+ * the XCDs the way it expects; once per device (on the first call of any
+ * entry point that reads) the library reads 8 tokens through it and through
+ * the wide path and keeps it only if every workgroup fits, no bounded wait
+ * expired and the two outputs agree to 4e-6 of their largest value.  The
+ * pages' reads check themselves the same way, once per card, bit for bit
+ * against the plain variant ("#315 hc: the multi-token hyper-connection read
+ * split finer", Exactness).  One line per device goes to stderr unless
+ * HC_LOG=0; HC_SELFCHECK_WAIT_TICKS lowers the bounded waits' limit for the
+ * check (ticks of the 100 MHz clock), which forces the fallback.  Runs the
+ * check on the default stream if it has not run yet (not under capture).
+ * Returns HC_OK or an HC_ERR_* code.
+ */
+HC_API int hc_short_window_on(int* on);
 
 /* Text for a status code (static storage; never NULL). */
 HC_API const char* hc_status_string(int status);

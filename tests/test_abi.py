@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == ["hc_read", "hc_read_commit", "hc_status_string", "hc_last_hip_error", "hc_dims",
-                     "hc_timeouts", "hc_release"]
+    assert names == ["hc_read", "hc_read_commit", "hc_short_window_on", "hc_status_string",
+                     "hc_last_hip_error", "hc_dims", "hc_timeouts", "hc_release"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -92,6 +92,9 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     for fn in (binding.hc_read, binding.hc_read_commit):
         st = fn(1, good, good, good, good, good, good, good, good, 0)
         assert st == binding.HC_ERR_DEVICE
+    with pytest.raises(binding.HCError):
+        binding.hc_short_window_on()
+    assert binding.library().hc_short_window_on(None) == binding.HC_ERR_ARG
 
 
 def test_python_read_refuses_cpu_tensors(lib):

@@ -124,6 +124,50 @@ def test_commit_writes_the_pending_update(T, pending):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+def test_short_window_check_passes():
+    """The start-up check keeps the short-window kernel on an MI355X."""
+    _case("start-up check of the short-window kernel")
+    from hyper_connection_residual_amd import binding
+    assert binding.hc_short_window_on()
+
+
+_FALLBACK_CHILD = """
+import sys
+sys.path.insert(0, '.')
+from hyper_connection_residual_amd import binding, workloads as wl
+from oracle import oracle as orc
+from tests.hc_testlib import assert_parity, hip_read, to_device
+assert not binding.hc_short_window_on(), 'the forced check should fail'
+for T in (1, 4, 8, 16):
+    print('[child] T=%d on the wide path' % T, flush=True)
+    inp = wl.config_inputs(2, T=T, weight_set=4)
+    gpu = hip_read(to_device(inp))
+    ref = orc.oracle_read(inp.R, inp.w_norm, inp.W_down, inp.W_up, inp.pending, threads=8)
+    assert_parity(gpu, ref, label='fallback T=%d' % T)
+print('[child] ok', flush=True)
+"""
+
+
+def test_forced_check_failure_falls_back_to_the_wide_path():
+    """With the bounded waits' limit forced to 0 ticks for the start-up check
+    (every wait of the check's read gives up at its first miss, and the
+    kernel still ends normally), the check fails, the library logs it, and
+    windows of up to 24 tokens then run the wide path, still at parity.  Run
+    in a child process, since the check runs once per process."""
+    import os
+    import subprocess
+    import sys
+    _case("forced start-up check failure (child process, HC_SELFCHECK_WAIT_TICKS=0)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, HC_SELFCHECK_WAIT_TICKS="0", HC_LOG="1")
+    r = subprocess.run([sys.executable, "-c", _FALLBACK_CHILD], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    assert "[child] ok" in r.stdout
+    assert "the short-window read is OFF" in r.stderr
+
+
 def test_outlier_channels_full_oracle():
     _case("config 3 distributions at T=300 (several tiles, ragged tail), full oracle")
     inp = wl.config_inputs(3, T=300)
