@@ -266,17 +266,18 @@ def main():
     if not args.no_prefill:
         from hyper_connection_residual_amd import workloads as wl
 
-        def time_wide(T, R, P, w_norm, Wd, Wu, reps):
+        def time_wide(T, R, P, w_norm, Wd, Wu, reps, fn=None):
+            fn = fn or binding.hc_read
             o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
                  torch.empty((T, 2560), dtype=torch.int16, device=dev),
                  torch.empty((T, 2560), dtype=torch.int16, device=dev))
             for _ in range(3):
-                binding.hc_read(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+                fn(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(reps):
-                binding.hc_read(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
+                fn(T, R, P, w_norm, Wd, Wu, o[0], o[1], o[2], stream.cuda_stream)
             b.record(stream)
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / reps
@@ -294,6 +295,11 @@ def main():
             r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 20 if inp.T <= 2048 else 10)
             prefill_all["T%d" % inp.T] = r
             print("# prefill T=%d: %.4f ms per read" % (inp.T, r["ms_per_read"]), file=sys.stderr, flush=True)
+            if inp.T == 8192:  # the bf16-lo mode (hc_read_bf16_lo), its own error-bound contract
+                r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 10, fn=binding.hc_read_bf16_lo)
+                prefill_all["T8192_bf16_lo"] = r
+                print("# prefill T=8192, bf16 lo: %.4f ms per read" % r["ms_per_read"], file=sys.stderr,
+                      flush=True)
             del R
         # config 5 (T = 32768 with pending): the same distributions drawn on the
         # device (R ~ Student-t(4) / sqrt(2), pending ~ N(0, 0.05)); the read's

@@ -27,6 +27,7 @@ _P = ctypes.c_void_p
 SIGNATURES = {
     "hc_read": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_read_commit": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hc_read_bf16_lo": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_short_window_on": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)]),
     "hc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hc_last_hip_error": (ctypes.c_int, []),
@@ -95,6 +96,15 @@ def hc_read_commit(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out
     return library().hc_read_commit(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
                                     _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
                                     _stream(stream))
+
+
+def hc_read_bf16_lo(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, stream=None):
+    """hc_read_bf16_lo of the C ABI: the wide path's up projection on bf16(lo).
+
+    Returns the status code (0 = HC_OK)."""
+    return library().hc_read_bf16_lo(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
+                                     _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
+                                     _stream(stream))
 
 
 def hc_short_window_on() -> bool:

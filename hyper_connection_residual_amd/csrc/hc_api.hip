@@ -220,8 +220,8 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     if (e == hipSuccess)
         e = hc::launch_decode(T, dR, dP, dw, dWd, dWu, m1, img, img + nout, nullptr, ws->dec, hs, ticks);
     if (e == hipSuccess)
-        e = hc::launch_prefill(T, dR, dP, dw, dWd, dWu, m2, img + 2 * nout, img + 3 * nout, nullptr, ws->wide_base,
-                               hc::kPrefillChunk, hs);
+        e = hc::launch_prefill(T, dR, dP, dw, dWd, dWu, m2, img + 2 * nout, img + 3 * nout, nullptr, false,
+                               ws->wide_base, hc::kPrefillChunk, hs);
     if (e == hipSuccess) e = hipMemcpyAsync(&expired, ws->dec.timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost, hs);
     if (e == hipSuccess) e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
     if (e == hipSuccess) e = hipMemcpyAsync(a.data(), m1, 4 * nout, hipMemcpyDeviceToHost, hs);
@@ -264,10 +264,11 @@ int short_window_on(int dev, Workspace* ws, bool* on)
     return HC_OK;
 }
 
-// The read of hc_read and hc_read_commit; R_commit is NULL or R.
+// The read of hc_read, hc_read_commit and hc_read_bf16_lo; R_commit is NULL
+// or R; bf16_lo selects the fast numerics of the wide path.
 int read_impl(int64_t T, const float* R, const float* pending, const float* w_norm, const uint16_t* W_down,
               const uint16_t* W_up, float* out_mixed, uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit,
-              void* stream)
+              void* stream, bool bf16_lo = false)
 {
     if (T < 1 || !R || !w_norm || !W_down || !W_up || !out_mixed || !out_bf16 || !out_fp16)
         return HC_ERR_ARG;
@@ -314,7 +315,7 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
     if (st != HC_OK)
         return st;
     hipError_t e = hc::launch_prefill(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R_commit,
-                                      ws->wide_base, hc::kPrefillChunk, hs);
+                                      bf16_lo, ws->wide_base, hc::kPrefillChunk, hs);
     return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
 }
 
@@ -334,6 +335,13 @@ HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float
                           uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
 {
     return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R, stream);
+}
+
+HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, const float* w_norm,
+                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                           uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
+{
+    return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, nullptr, stream, true);
 }
 
 HC_API int hc_short_window_on(int* on)

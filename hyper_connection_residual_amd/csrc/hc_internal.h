@@ -80,9 +80,10 @@ constexpr int kPrefillChunk = 4096;
 
 size_t prefill_scratch_bytes(int chunk);
 
+// bf16_lo: the up projection takes lo rounded to bf16 (hc_read_bf16_lo).
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, void* scratch,
-                          int chunk, hipStream_t stream);
+                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, bool bf16_lo,
+                          void* scratch, int chunk, hipStream_t stream);
 
 }  // namespace hc

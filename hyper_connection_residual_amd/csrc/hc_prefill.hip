@@ -468,7 +468,7 @@ constexpr int kUpStage = kUpWChunks + kLoTile;   // 1536 chunks
 constexpr int kUpSlots = 3;
 constexpr int kUpLoads = (kUpWChunks + kLoTile) / 64 / 4;  // wave instructions per stage and wave (6)
 
-template <bool HAS_P>
+template <bool HAS_P, bool BF16_LO>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* R,
@@ -543,10 +543,14 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         wa[7] = ds_read16_off<7168>(wb);
         asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
         asm volatile("" : "+v"(lv[0]), "+v"(lv[1]));
-        uint32_t hi[8], mi[8], l3[8];
+        uint32_t hi[8], mi[8] = {}, l3[8] = {};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            split3(__uint_as_float(lv[e >> 2][e & 3]), hi[e], mi[e], l3[e]);
+        for (int e = 0; e < 8; ++e) {
+            if (BF16_LO)  // the fast mode: lo rounded to bf16 (nearest even), one piece
+                hi[e] = __builtin_bit_cast(uint16_t, (__bf16)__uint_as_float(lv[e >> 2][e & 3]));
+            else
+                split3(__uint_as_float(lv[e >> 2][e & 3]), hi[e], mi[e], l3[e]);
+        }
         u32x4 y[3];
         y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
         y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
@@ -568,7 +572,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
             asm volatile("" : "+v"(wa[k]));
         // panel block index k = 4 s + cb
 #pragma unroll
-        for (int p = 2; p >= 0; --p)
+        for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 acc[k & 3][k >> 2] = mfma16(wa[k], y[p], acc[k & 3][k >> 2]);
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         for (int k = 0; k < 8; ++k)
             asm volatile("" : "+v"(wn[k]));
 #pragma unroll
-        for (int p = 2; p >= 0; --p)
+        for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 acc[k & 3][2 + (k >> 2)] = mfma16(wn[k], y[p], acc[k & 3][2 + (k >> 2)]);
@@ -764,8 +768,8 @@ size_t prefill_scratch_bytes(int chunk)
 
 hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float* w_norm,
                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
-                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, void* scratch,
-                          int chunk, hipStream_t stream)
+                          uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, bool bf16_lo,
+                          void* scratch, int chunk, hipStream_t stream)
 {
     const size_t slots = part_slots(chunk);
     float* part = static_cast<float*>(scratch);  // [S][Tc][320]
@@ -789,12 +793,10 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
             return e;
         const int grid3 = 8 * kGroupsPerXcd * tiles;
         float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
-        if (Pc)
-            hipLaunchKernelGGL(prefill_upmix<true>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
-                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
-        else
-            hipLaunchKernelGGL(prefill_upmix<false>, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc,
-                               out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
+        auto* up = Pc ? (bf16_lo ? prefill_upmix<true, true> : prefill_upmix<true, false>)
+                      : (bf16_lo ? prefill_upmix<false, true> : prefill_upmix<false, false>);
+        hipLaunchKernelGGL(up, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc, out_mixed + out_off,
+                           out_bf16 + out_off, out_fp16 + out_off, Cc);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -127,6 +127,23 @@ HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float
                    uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
 
 /*
+ * hc_read_bf16_lo -- hc_read with the pages' prefill numerics on the wide
+ * path: the up projection takes lo rounded to bf16 (nearest even) and runs
+ * one bf16 matrix product with fp32 accumulation, as the fused up + mix of
+ * "#1370 prefill: opt-in STRATA_HC_UPMIX=1 on CUDA", What it does (BF16 mma
+ * with FP32 accumulation), instead of the exact three-piece split of lo.  The
+ * norm, the down projection and lo itself are unchanged, and windows of up to
+ * 24 tokens (the short-window kernel) give hc_read's result.
+ * Its contract is an error bound, not hc_read's 2e-6: every mixed value is
+ * within 2^-8 * sum_s |R'[t][s][c]| * sum_j |W_up[s*2560+c][j]| * |lo[t][j]|
+ * of the exact read (the bf16 rounding of each lo value), plus hc_read's
+ * fp32 budget.  Arguments, layouts and errors as for hc_read.
+ */
+HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, const float* w_norm,
+                    const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                    uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
+
+/*
  * hc_short_window_on -- *on = 1 if the current device reads windows of up to
  * 24 tokens with the short-window kernel, 0 if they take the wide path.  The
  * kernel's hand-offs need its 256 workgroups resident together and placed on

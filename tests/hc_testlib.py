@@ -34,9 +34,10 @@ def to_device(inp, device="cuda"):
                 W_down=t(inp.W_down.view(np.int16)), W_up=t(inp.W_up.view(np.int16)))
 
 
-def hip_read(dev, stream=None, commit=False):
-    """The read through the C ABI (hc_read, or hc_read_commit, which also
-    updates dev["R"] in place); returns numpy (mixed f32, bf16 bits, fp16 bits)."""
+def hip_read(dev, stream=None, commit=False, bf16_lo=False):
+    """The read through the C ABI (hc_read; hc_read_commit, which also updates
+    dev["R"] in place; or hc_read_bf16_lo); returns numpy (mixed f32, bf16
+    bits, fp16 bits)."""
     import torch
     from hyper_connection_residual_amd import binding
     R = dev["R"]
@@ -44,7 +45,7 @@ def hip_read(dev, stream=None, commit=False):
     mixed = torch.empty((T, C), dtype=torch.float32, device=R.device)
     b16 = torch.empty((T, C), dtype=torch.int16, device=R.device)
     f16 = torch.empty((T, C), dtype=torch.int16, device=R.device)
-    fn = binding.hc_read_commit if commit else binding.hc_read
+    fn = binding.hc_read_commit if commit else binding.hc_read_bf16_lo if bf16_lo else binding.hc_read
     st = fn(T, R, dev["pending"], dev["w_norm"], dev["W_down"], dev["W_up"], mixed, b16, f16, stream)
     assert st == 0, "hc_read failed: %s" % binding.hc_status_string(st)
     torch.cuda.synchronize()

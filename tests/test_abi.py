@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == ["hc_read", "hc_read_commit", "hc_short_window_on", "hc_status_string",
+    assert names == ["hc_read", "hc_read_commit", "hc_read_bf16_lo", "hc_short_window_on", "hc_status_string",
                      "hc_last_hip_error", "hc_dims", "hc_timeouts", "hc_release"]
 
 
@@ -63,7 +63,7 @@ def test_status_strings(lib):
     assert binding.hc_status_string(99) == "unknown status"
 
 
-@pytest.mark.parametrize("entry", ["hc_read", "hc_read_commit"])
+@pytest.mark.parametrize("entry", ["hc_read", "hc_read_commit", "hc_read_bf16_lo"])
 def test_argument_checks_happen_before_any_hip_call(lib, entry):
     from hyper_connection_residual_amd import binding
     fn = getattr(binding, entry)
@@ -89,7 +89,7 @@ def test_argument_checks_happen_before_any_hip_call(lib, entry):
 def test_no_device_is_an_error_not_a_fallback(lib):
     from hyper_connection_residual_amd import binding
     good = 0x10000
-    for fn in (binding.hc_read, binding.hc_read_commit):
+    for fn in (binding.hc_read, binding.hc_read_commit, binding.hc_read_bf16_lo):
         st = fn(1, good, good, good, good, good, good, good, good, 0)
         assert st == binding.HC_ERR_DEVICE
     with pytest.raises(binding.HCError):

@@ -168,6 +168,49 @@ def test_forced_check_failure_falls_back_to_the_wide_path():
     assert "the short-window read is OFF" in r.stderr
 
 
+def _bf16_lo_bound(inp, tokens, lo):
+    """2^-8 * sum_s |R'| * (|W_up| @ |lo|): what rounding each lo value to
+    bf16 (nearest even, relative error <= 2^-8) can move mixed by."""
+    n, C = inp.w_norm.shape
+    R = inp.R[tokens].astype(np.float32)
+    if inp.pending is not None:
+        R = R + inp.pending[tokens].astype(np.float32)
+    Rp = np.abs(R.astype(np.float64))                               # [t, n, C]
+    Wu = np.abs((inp.W_up.astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [n C, r], exact
+    A = (np.abs(lo) @ Wu.T).reshape(len(tokens), n, C)               # [t, n, C]
+    return 2.0 ** -8 * np.sum(Rp * A, axis=1)                        # [t, C]
+
+
+@pytest.mark.parametrize("T, pending", [(300, False), (4097, True)])
+def test_bf16_lo_mode_within_its_bound(T, pending):
+    """hc_read_bf16_lo: every mixed value within the bf16-rounding bound of
+    the exact read (plus hc_read's fp32 budget), and visibly not the exact
+    read (the fast path ran).  T = 300: every token; T = 4097 (two chunks):
+    a sample."""
+    _case("bf16-lo mode: T=%d, pending=%s" % (T, pending))
+    inp = wl.config_inputs(5 if pending else 3, T=T, seed=T + 1)
+    gpu = hip_read(to_device(inp), bf16_lo=True)
+    toks = np.arange(T) if T <= 300 else np.array(sorted(set(_sample_tokens(T, k=20, seed=T).tolist()) |
+                                                        {0, 4095, 4096}))
+    R = inp.R[toks]
+    P = None if inp.pending is None else inp.pending[toks]
+    ref, lo = orc.oracle_read(R, inp.w_norm, inp.W_down, inp.W_up, P, eps=inp.eps, threads=8, want_lo=True)
+    err = np.abs(gpu[0][toks].astype(np.float64) - ref)
+    bound = _bf16_lo_bound(inp, toks, lo) + 2e-6 * np.max(np.abs(ref))
+    assert np.all(err <= bound), "worst excess %.3e" % np.max(err - bound)
+    assert np.max(err) > 2e-6 * np.max(np.abs(ref)), "bf16(lo) should move the result"
+
+
+def test_bf16_lo_mode_short_windows_are_exact():
+    """Up to 24 tokens hc_read_bf16_lo is the short-window read: hc_read's bits."""
+    _case("bf16-lo mode at T=8 and T=24 against hc_read")
+    for T in (8, 24):
+        dev = to_device(wl.config_inputs(2, T=T, weight_set=6))
+        for a, b in zip(hip_read(dev, bf16_lo=True), hip_read(dev)):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
 def test_outlier_channels_full_oracle():
     _case("config 3 distributions at T=300 (several tiles, ragged tail), full oracle")
     inp = wl.config_inputs(3, T=300)
