@@ -35,7 +35,7 @@ TOKEN_BYTES_P = 4 * 2560 * 4 * 2 + 2560 * (4 + 2 + 2)  # R and pending read, mix
 HBM_PEAK_GBPS = 8000.0
 N_SETS = 48
 TS = list(range(1, 9))
-WINDOWS = [9, 12, 16, 24, 25, 32, 48, 64]  # windows above 8 tokens, timed beside the sweep
+WINDOWS = [9, 12, 16, 17, 24, 32, 33, 48, 64]  # windows above 8 tokens, timed beside the sweep
 
 
 def parse():
@@ -176,8 +176,8 @@ def main():
     print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
     del step_graphs
 
-    # ---- windows of 9..64 tokens (up to 24: one short-window launch per 8
-    # tokens; beyond: the wide path), eager, weights rotated over the 48 sets
+    # ---- windows of 9..64 tokens (up to 16: one short-window launch, up to
+    # 32: two; beyond: the wide path), eager, weights rotated over the 48 sets
     from hyper_connection_residual_amd import workloads as wl
     us_windows = {}
     for T in WINDOWS:

@@ -1,7 +1,7 @@
 // hc_api.hip -- host side of the C ABI declared in include/hc.h: argument
 // checks, per-(device, stream) scratch workspaces, the start-up check of the
-// short-window kernel, and dispatch to the short-window (T <= 24, in launches
-// of up to 8 tokens) and wide (prefill) kernels.
+// short-window kernel, and dispatch to the short-window (T <= 32, in launches
+// of up to 16 tokens) and wide (prefill) kernels.
 #include "hc.h"
 #include "hc_internal.h"
 
@@ -162,7 +162,7 @@ struct CheckRng {
 // needs neither) and keeps it only if (a) every workgroup fits, (b) no
 // bounded wait expired and (c) the two outputs agree to 4e-6 of their largest
 // value (each is within 2e-6 of the exact read).  Otherwise windows of up to
-// 24 tokens take the wide path.  The bounded waits' limit can be lowered with
+// 32 tokens take the wide path.  The bounded waits' limit can be lowered with
 // HC_SELFCHECK_WAIT_TICKS (ticks of the 100 MHz clock) to force the
 // fallback.  One line per device goes to stderr (HC_LOG=0 silences it).
 int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t why_len)
@@ -183,7 +183,7 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     int st = wide_workspace(ws);
     if (st != HC_OK)
         return st;
-    constexpr int T = hc::kDecMaxT;
+    constexpr int T = 8;
     const size_t nin = (size_t)T * hc::kD, nw = (size_t)hc::kRank * hc::kD, nout = (size_t)T * hc::kWidth;
     CheckRng rng;
     std::vector<float> R(nin), P(nin), w(hc::kD);
@@ -243,7 +243,7 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     return HC_OK;
 }
 
-// Whether windows of up to 24 tokens use the short-window kernel on `dev`;
+// Whether windows of up to 32 tokens use the short-window kernel on `dev`;
 // the check runs on the first call for the device.
 int short_window_on(int dev, Workspace* ws, bool* on)
 {
@@ -260,7 +260,7 @@ int short_window_on(int dev, Workspace* ws, bool* on)
     g_short_window.emplace(dev, *on);
     if (log_enabled())
         std::fprintf(stderr, "hc: device %d: the short-window read is %s (start-up check: %s)%s\n", dev,
-                     *on ? "on" : "OFF", why, *on ? "" : "; windows of up to 24 tokens take the wide path");
+                     *on ? "on" : "OFF", why, *on ? "" : "; windows of up to 32 tokens take the wide path");
     return HC_OK;
 }
 

@@ -1,4 +1,4 @@
-// hc_decode.hip -- the hyper-connection read for short windows (T <= 8 tokens)
+// hc_decode.hip -- the hyper-connection read for short windows (T <= 16 tokens)
 // as ONE kernel launch on gfx950.
 //
 // What it computes is the read of "#315 hc: the multi-token hyper-connection
@@ -105,6 +105,33 @@ __host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
     return ((y * kDecXcds + xs) * 16 + us) * kLoBlock + t * kLoRows + r;
 }
 
+// Short-window MFMA blocks put (piece, token) pairs on the 16 A rows: row
+// p T + t holds piece p (0 hi, 1 mid, 2 lo3) of token t.  kChains: MFMA chains
+// per block (1 when all 3 T rows fit; up to 8 tokens 2: pieces 0-1, then
+// piece 2; beyond, 3: one per piece).  kPackRows: the A rows chain 0 carries.
+template <int T>
+constexpr int kChains = 3 * T <= 16 ? 1 : (T <= 8 ? 2 : 3);
+template <int T>
+constexpr int kPackRows = kChains<T> == 1 ? 3 * T : (kChains<T> == 2 ? 2 * T : T);
+// First plane row (p T + t) and row count of chain c.
+template <int T>
+__host__ __device__ constexpr int chain_base(int c)
+{
+    return c == 0 ? 0 : (kChains<T> == 3 ? c * T : 2 * T);
+}
+template <int T>
+__host__ __device__ constexpr int chain_rows(int c)
+{
+    return c == 0 ? kPackRows<T> : T;
+}
+// Chains' room in the LDS product blocks (at least 2, as laid out for 1..8 tokens).
+template <int T>
+constexpr int kCombChains = kChains<T> < 2 ? 2 : kChains<T>;
+// Token slots of a partial-dot row in scratch: 8 (two rows per 128-byte
+// line) up to 8 tokens, else 16 (one row per line).
+template <int T>
+constexpr int kTokSlots = T <= 8 ? 8 : 16;
+
 // LDS map (bytes): both weight tiles, the y planes [3 T][kYRow] bf16, the
 // token sums of squares of the items [T][80] fp32, the down product blocks
 // [6][2 chains][64] f32x4, the lo planes [3 T][kLoRow] bf16, R' of the up
@@ -113,10 +140,10 @@ constexpr size_t kOffUTile = 16 * kTileChunks;
 constexpr size_t kOffY = 2 * 16 * kTileChunks;
 template <int T> constexpr size_t kOffSs = kOffY + 2 * 3 * T * kYRow;
 template <int T> constexpr size_t kOffComb = kOffSs<T> + 4 * T * kStageItems;
-template <int T> constexpr size_t kOffLo = kOffComb<T> + 6 * 2 * 64 * 16;
+template <int T> constexpr size_t kOffLo = kOffComb<T> + 6 * kCombChains<T> * 64 * 16;
 template <int T> constexpr size_t kOffRp = kOffLo<T> + 2 * 3 * T * kLoRow;
 template <int T> constexpr size_t kOffUComb = kOffRp<T> + 4 * T * kUpRows;
-template <int T> constexpr size_t kLdsBytes = kOffUComb<T> + 3 * 2 * 64 * 16;
+template <int T> constexpr size_t kLdsBytes = kOffUComb<T> + 3 * kCombChains<T> * 64 * 16;
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
 {
@@ -138,14 +165,6 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
     lo3 = __float_as_uint(r2) >> 16;
 }
 
-// Short-window MFMA blocks put (piece, token) pairs on the 16 A rows: row
-// p T + t holds piece p (0 hi, 1 mid, 2 lo3) of token t.  kChains: MFMA chains
-// per block (1 when all 3 T rows fit, else 2: pieces 0-1, then piece 2 on rows
-// 0..T-1).  kPackRows: the A rows chain 0 carries.
-template <int T>
-constexpr int kChains = 3 * T <= 16 ? 1 : 2;
-template <int T>
-constexpr int kPackRows = kChains<T> == 1 ? 3 * T : 2 * T;
 
 // Product-block element (piece p, token t; column = the lane's n) of block w,
 // from blocks stored in LDS as [block][chain][64 lanes] f32x4 (the MFMA's own
@@ -153,8 +172,8 @@ constexpr int kPackRows = kChains<T> == 1 ? 3 * T : 2 * T;
 template <int T>
 __device__ __forceinline__ float packed_at(const float* cf, int w, int p, int t, int n)
 {
-    const int c = (kChains<T> == 2 && p == 2) ? 1 : 0;
-    const int i = c ? t : p * T + t;
+    const int c = kChains<T> == 3 ? p : ((kChains<T> == 2 && p == 2) ? 1 : 0);
+    const int i = kChains<T> == 3 ? t : (c ? t : p * T + t);
     return cf[((w * kChains<T> + c) * 64 + n + 16 * (i >> 2)) * 4 + (i & 3)];
 }
 // The three pieces' products of token t summed: hi + (mid + lo3).
@@ -300,12 +319,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16,
     float* R_commit, long long wait_ticks)
 {
-    static_assert(T >= 1 && T <= kDecMaxT, "short-window kernel takes 1..8 tokens");
+    static_assert(T >= 1 && T <= kDecMaxT && kDecMaxT == 16, "short-window kernel takes 1..16 tokens");
     static_assert(kDecRowsPerXcd * kRowChunks == kTileChunks && kUpRows * kRowChunks == kTileChunks,
                   "both tiles are 1600 chunks");
     static_assert(kWidth % kDecDownCols == 0 && kWidth / kDecDownCols == 8, "8 down tiles per stream");
     static_assert(kDecXcds * kDecRowsPerXcd == kRank && kDecWGs * kDecUpCols == kWidth, "cover");
-    static_assert(kStageItems * kDecMaxT <= 2 * kDecThreads && kUpRows * kDecMaxT <= kDecThreads, "passes");
+    static_assert(kStageItems * kDecMaxT <= 3 * kDecThreads && kUpRows * kDecMaxT <= 2 * kDecThreads, "passes");
     static_assert(kDecReducers <= 16 && kDecRedRows == 3 && kDecWgPerXcd == 32, "reducer layout");
     static_assert(kLdsBytes<T> <= 160 * 1024, "LDS");
     __shared__ __align__(16) uint4 lds[kLdsBytes<T> / 16];
@@ -387,27 +406,42 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //     fetching the line from memory.
     uint32_t touched = 0, touched2 = 0;
     if (wave == 0 && reducer) {
-        const int src = lane & 31, k = lane >> 5;  // k 0, 1: partial lines of rows 3 u and 3 u + 2
-        const int row = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
-        touched = *reinterpret_cast<const uint32_t*>(
-            s.part + (((size_t)x * kDecWgPerXcd + src) * kDecRowsPerXcd + row) * kDecMaxT);
-        touched2 = *reinterpret_cast<const uint32_t*>(s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
+        const int src = lane & 31, k = lane >> 5;
+        const size_t prow = ((size_t)x * kDecWgPerXcd + src) * kDecRowsPerXcd;
+        if constexpr (T <= 8) {
+            // k 0, 1: the lines of rows 3 u and 3 u + 2 (two rows per line)
+            const int row = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
+            touched = *reinterpret_cast<const uint32_t*>(s.part + (prow + row) * kTokSlots<T>);
+            touched2 = *reinterpret_cast<const uint32_t*>(s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
+        } else {
+            // one row per line: rows 3 u + k, then row 3 u + 2 (k = 0) or the
+            // sums of squares (k = 1)
+            const int r0 = kDecRedRows * u + k, r2 = kDecRedRows * u + 2;
+            touched = *reinterpret_cast<const uint32_t*>(s.part + (prow + r0) * kTokSlots<T>);
+            touched2 = *reinterpret_cast<const uint32_t*>(
+                k == 0 ? s.part + (prow + (r2 < kDecRowsPerXcd ? r2 : kDecRowsPerXcd - 1)) * kTokSlots<T>
+                       : s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
+        }
     }
     // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
     //     and R and pending of those 40 (stream, column) pairs, for the mix
-    float mr = 0.f, mp = 0.f;
+    constexpr int kUpPasses = (kUpRows * T + kDecThreads - 1) / kDecThreads;  // 1, or 2 above 12 tokens
+    float mr[kUpPasses], mp[kUpPasses];
     auto issue_up = [&]() {
         for (int q = wave; q < kTileInstr; q += 8) {
             int row, j;
             tile_lane<kRowChunks>(q, lane, row, j);
             dma16(W_up + (size_t)((row & 3) * kWidth + c0 + (row >> 2)) * kRank + 8 * j, utile + 64 * q);
         }
-        const int it = threadIdx.x;
-        const int itc = it < kUpRows * T ? it : 0;
-        const int at = itc / kUpRows, row = itc - at * kUpRows;
-        const size_t o = (size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2);
-        mr = R[o];
-        mp = Pm[o];
+#pragma unroll
+        for (int pp = 0; pp < kUpPasses; ++pp) {
+            const int it = threadIdx.x + kDecThreads * pp;
+            const int itc = it < kUpRows * T ? it : 0;
+            const int at = itc / kUpRows, row = itc - at * kUpRows;
+            const size_t o = (size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2);
+            mr[pp] = R[o];
+            mp[pp] = Pm[o];
+        }
     };
 
     // (6) y = R' * w_norm (unscaled: the norm is folded into the reduction),
@@ -453,42 +487,64 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
         // all operands first (one LDS latency, not five); A rows past the
         // pieces re-read row 0: they only feed D rows nobody reads
-        const int r0 = m < kPackRows<T> ? m : 0;
-        const int r1 = 2 * T + (m < T ? m : 0);
-        uint4 wb[5], a0[5], a1[5];
+        const int r0 = chain_base<T>(0) + (m < chain_rows<T>(0) ? m : 0);
+        const int r1 = chain_base<T>(1) + (m < chain_rows<T>(1) ? m : 0);
+        const int r2 = chain_base<T>(2) + (m < chain_rows<T>(2) ? m : 0);
+        uint4 wb[5], a0[5], a1[5], a2[5];
 #pragma unroll
         for (int qq = 0; qq < 5; ++qq) {
             const int q = 5 * kh + qq;
             const int col = 32 * q + 8 * g;
             wb[qq] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
             a0[qq] = *reinterpret_cast<const uint4*>(&ypl[r0 * kYRow + col]);
-            if (kChains<T> == 2)
+            if (kChains<T> >= 2)
                 a1[qq] = *reinterpret_cast<const uint4*>(&ypl[r1 * kYRow + col]);
+            if (kChains<T> == 3)
+                a2[qq] = *reinterpret_cast<const uint4*>(&ypl[r2 * kYRow + col]);
         }
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
         for (int qq = 0; qq < 5; ++qq) {
             acc0 = mfma16(a0[qq], wb[qq], acc0);
-            if (kChains<T> == 2)
+            if (kChains<T> >= 2)
                 acc1 = mfma16(a1[qq], wb[qq], acc1);
+            if (kChains<T> == 3)
+                acc2 = mfma16(a2[qq], wb[qq], acc2);
         }
         comb[(wave * kChains<T>) * 64 + lane] = acc0;
-        if (kChains<T> == 2)
+        if (kChains<T> >= 2)
             comb[(wave * kChains<T> + 1) * 64 + lane] = acc1;
+        if (kChains<T> == 3)
+            comb[(wave * kChains<T> + 2) * 64 + lane] = acc2;
     } else if (wave == 6) {
         // (7') meanwhile, the slice's sum of squares per token: lane 8 t + p
         //      sums 10 of token t's 80 item sums, then the 8 lanes combine theirs
-        const int tt = lane >> 3, p = lane & 7;
-        float ss = 0.f;
-        if (tt < T) {
+        if constexpr (T <= 8) {
+            const int tt = lane >> 3, p = lane & 7;
+            float ss = 0.f;
+            if (tt < T) {
 #pragma unroll
-            for (int f = 0; f < kStageItems / 8; ++f)
-                ss += sspart[tt * kStageItems + (kStageItems / 8) * p + f];
+                for (int f = 0; f < kStageItems / 8; ++f)
+                    ss += sspart[tt * kStageItems + (kStageItems / 8) * p + f];
+            }
+            ss = sum8(ss);
+            if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
+                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + 8 * p + tt],
+                            tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
+        } else {
+            // lane 4 t + p sums 20 of token t's 80 item sums, then the 4
+            // lanes combine theirs; words 0..15: tokens (0 past T)
+            const int tt = lane >> 2, p = lane & 3;
+            float ss = 0.f;
+            if (tt < T) {
+#pragma unroll
+                for (int f = 0; f < kStageItems / 4; ++f)
+                    ss += sspart[tt * kStageItems + (kStageItems / 4) * p + f];
+            }
+            ss = sum4(ss);
+            if (p == 0)
+                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + tt], tag_f32(ss, xcd_tag(gen, rot)));
         }
-        ss = sum8(ss);
-        if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
-            st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + 8 * p + tt],
-                        tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
     }
     HC_PROBE(2, threadIdx.x == 0);
     wg_barrier();  // Bc1: every product block in LDS
@@ -497,13 +553,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         // (8) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g, into
         //     the XCD's L2: per K half hi + (mid + lo3), then the two halves
         //     (all 8 token slots, whole lines; slots >= T hold 0)
+        //     (above 8 tokens each lane also takes token t + 8: 16 slots)
         const float* cf = reinterpret_cast<const float*>(comb);
         const int nb = wave % 3, t = 4 * (wave / 3) + g;
         const int row = 16 * nb + n;
         if (row < kDecRowsPerXcd) {
-            const float v = t < T ? piece_sum<T>(cf, nb, t, n) + piece_sum<T>(cf, nb + 3, t, n) : 0.f;
-            st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kDecMaxT + t,
-                        tag_f32(v, xcd_tag(gen, rot)));
+#pragma unroll
+            for (int h = 0; h < kTokSlots<T> / 8; ++h) {
+                const int th = t + 8 * h;
+                const float v = th < T ? piece_sum<T>(cf, nb, th, n) + piece_sum<T>(cf, nb + 3, th, n) : 0.f;
+                st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kTokSlots<T> + th,
+                            tag_f32(v, xcd_tag(gen, rot)));
+            }
         }
     }
     HC_PROBE(3, threadIdx.x == 0);
@@ -539,7 +600,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const int row = kDecRedRows * u + k;
             const bool valid = k < kDecRedRows && row < kDecRowsPerXcd;
             const int rowc = valid ? row : kDecRedRows * u;  // (a row of this reducer, read and discarded)
-            const int pa = (pa0 + rowc) * kDecMaxT, pb = (pb0 + rowc) * kDecMaxT;
+            const int pa = (pa0 + rowc) * kTokSlots<T>, pb = (pb0 + rowc) * kTokSlots<T>;
             uint4 wa_[NP], wb_[NP], qa_[NP], qb_[NP];
             [[maybe_unused]] int rounds = 0;
             while (true) {
@@ -587,31 +648,42 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
 #pragma unroll
             for (int y = 0; y < kDecXcds; ++y)
-                if (src < kDecMaxT)
+                if (src < 8)
                     st_word(&s.lo[lo_word(y, x, u, src, k)], word);
         } else {
+            // token pairs: lane group k takes pairs k + 4 q (q < NQ: tokens
+            // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows
+            constexpr int NQ = kTokSlots<T> / 8;
             int pidx[kDecRedRows];
 #pragma unroll
             for (int rr = 0; rr < kDecRedRows; ++rr) {
                 const int row = kDecRedRows * u + rr;
-                pidx[rr] = (row < kDecRowsPerXcd ? row : kDecRowsPerXcd - 1) * kDecMaxT + 2 * k;
+                pidx[rr] = (row < kDecRowsPerXcd ? row : kDecRowsPerXcd - 1) * kTokSlots<T> + 2 * k;
             }
-            uint4 wa_[kDecRedRows], wb_[kDecRedRows], qa_, qb_;
+            uint4 wa_[kDecRedRows][NQ], wb_[kDecRedRows][NQ], qa_[NQ], qb_[NQ];
             [[maybe_unused]] int rounds = 0;
             while (true) {
                 ++rounds;
                 new_round();
 #pragma unroll
-                for (int rr = 0; rr < kDecRedRows; ++rr) {
-                    wa_[rr] = ld_words2(s.part, pa0 * kDecMaxT + pidx[rr]);
-                    wb_[rr] = ld_words2(s.part, pb0 * kDecMaxT + pidx[rr]);
-                }
-                qa_ = ld_words2(s.ssq, sa0 + 2 * k);
-                qb_ = ld_words2(s.ssq, sb0 + 2 * k);
-                bool ok = (qa_.y == htag) & (qa_.w == htag) & (qb_.y == htag) & (qb_.w == htag);
+                for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-                for (int rr = 0; rr < kDecRedRows; ++rr)
-                    ok = ok & (wa_[rr].y == htag) & (wa_[rr].w == htag) & (wb_[rr].y == htag) & (wb_[rr].w == htag);
+                    for (int rr = 0; rr < kDecRedRows; ++rr) {
+                        wa_[rr][q] = ld_words2(s.part, pa0 * kTokSlots<T> + pidx[rr] + 8 * q);
+                        wb_[rr][q] = ld_words2(s.part, pb0 * kTokSlots<T> + pidx[rr] + 8 * q);
+                    }
+                    qa_[q] = ld_words2(s.ssq, sa0 + 2 * k + 8 * q);
+                    qb_[q] = ld_words2(s.ssq, sb0 + 2 * k + 8 * q);
+                }
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    ok = ok & (qa_[q].y == htag) & (qa_[q].w == htag) & (qb_[q].y == htag) & (qb_[q].w == htag);
+#pragma unroll
+                    for (int rr = 0; rr < kDecRedRows; ++rr)
+                        ok = ok & (wa_[rr][q].y == htag) & (wa_[rr][q].w == htag) & (wb_[rr][q].y == htag) &
+                             (wb_[rr][q].w == htag);
+                }
                 if (__all(ok)) {
                     HC_COUNT(0, 0, rounds, lane == 0);
                     break;
@@ -624,23 +696,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 __builtin_amdgcn_s_sleep(1);
             }
             HC_PROBE(12, lane == 0);
-            float lo[kDecRedRows][2];  // [row][token 2 k + h], the same in all 16 lanes of k
+            float lo[kDecRedRows][NQ][2];  // [row][pair group][token], the same in all 16 lanes of k
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int q = 0; q < NQ; ++q)
 #pragma unroll
-                for (int rr = 0; rr < kDecRedRows; ++rr)
-                    lo[rr][h] = combine(__uint_as_float(h ? wa_[rr].z : wa_[rr].x),
-                                        __uint_as_float(h ? wb_[rr].z : wb_[rr].x),
-                                        __uint_as_float(h ? qa_.z : qa_.x), __uint_as_float(h ? qb_.z : qb_.x));
-            // lane src < 8 of group k writes row src / 2, token 2 k + src % 2
-            const int rr = src >> 1, h = src & 1, tok = 2 * k + h;
-            const float l0 = h ? lo[0][1] : lo[0][0], l1 = h ? lo[1][1] : lo[1][0], l2 = h ? lo[2][1] : lo[2][0];
-            const float mine = rr == 0 ? l0 : rr == 1 ? l1 : l2;
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int rr = 0; rr < kDecRedRows; ++rr)
+                        lo[rr][q][h] = combine(__uint_as_float(h ? wa_[rr][q].z : wa_[rr][q].x),
+                                               __uint_as_float(h ? wb_[rr][q].z : wb_[rr][q].x),
+                                               __uint_as_float(h ? qa_[q].z : qa_[q].x),
+                                               __uint_as_float(h ? qb_[q].z : qb_[q].x));
+            // lane src < 8 NQ of group k writes row (src / 2) % 4 (row 3:
+            // padding), token 2 k + src % 2 + 8 (src / 8)
+            const int rr = (src >> 1) & 3, h = src & 1, q = src >> 3, tok = 2 * k + h + 8 * q;
+            float mine = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+                for (int r3 = 0; r3 < kDecRedRows; ++r3)
+                    mine = (qq == q && r3 == rr) ? (h ? lo[r3][qq][1] : lo[r3][qq][0]) : mine;
             const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
             const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
 #pragma unroll
             for (int y = 0; y < kDecXcds; ++y)
-                if (src < 8)
+                if (src < 8 * NQ)
                     st_word(&s.lo[lo_word(y, x, u, tok, rr)], word);
         }
         HC_PROBE(13, lane == 0);
@@ -713,9 +793,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         HC_PROBE(7, wave == 0 && lane == 0);
     }
     wait_all_loads();  // the W_up tile and R' have landed
-    const float rprime = P ? mr + mp : mr;
-    if (threadIdx.x < kUpRows * T)
-        rpl[threadIdx.x] = rprime;  // it = 40 t + row
+    float rprime[kUpPasses];
+#pragma unroll
+    for (int pp = 0; pp < kUpPasses; ++pp) {
+        rprime[pp] = P ? mr[pp] + mp[pp] : mr[pp];
+        const int it = threadIdx.x + kDecThreads * pp;  // it = 40 t + row
+        if (it < kUpRows * T)
+            rpl[it] = rprime[pp];
+    }
     wg_barrier();  // B2: lo and R' staged, W_up tile complete
     HC_PROBE(8, threadIdx.x == 0);
     // (10') the pending write committed: R' of this workgroup's 40 (stream,
@@ -723,9 +808,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //      anywhere: every workgroup read them for its down part before it
     //      stored the partials that hop 2 has just waited for, and no other
     //      workgroup mixes these columns.
-    if (R_commit && P && threadIdx.x < kUpRows * T) {
-        const int at = threadIdx.x / kUpRows, row = threadIdx.x - at * kUpRows;
-        R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime;
+#pragma unroll
+    for (int pp = 0; pp < kUpPasses; ++pp) {
+        const int it = threadIdx.x + kDecThreads * pp;
+        if (R_commit && P && it < kUpRows * T) {
+            const int at = it / kUpRows, row = it - at * kUpRows;
+            R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime[pp];
+        }
     }
 
     if (wave < 3) {
@@ -736,29 +825,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         //      4 streams of a column
         const int row = wave < 2 ? 16 * wave + n : 32 + (n & 7);
         const int st = n & 3;
-        const int r0 = m < kPackRows<T> ? m : 0;
-        const int r1 = 2 * T + (m < T ? m : 0);
-        uint4 wb[10], a0[10], a1[10];
+        const int r0 = chain_base<T>(0) + (m < chain_rows<T>(0) ? m : 0);
+        const int r1 = chain_base<T>(1) + (m < chain_rows<T>(1) ? m : 0);
+        const int r2 = chain_base<T>(2) + (m < chain_rows<T>(2) ? m : 0);
+        uint4 wb[10], a0[10], a1[10], a2[10];
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             const int jc = 32 * q + 8 * g;
             wb[q] = utile[tile_pos<kRowChunks>(row, 4 * q + g)];
             a0[q] = *reinterpret_cast<const uint4*>(&lpl[r0 * kLoRow + jc]);
-            if (kChains<T> == 2)
+            if (kChains<T> >= 2)
                 a1[q] = *reinterpret_cast<const uint4*>(&lpl[r1 * kLoRow + jc]);
+            if (kChains<T> == 3)
+                a2[q] = *reinterpret_cast<const uint4*>(&lpl[r2 * kLoRow + jc]);
         }
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             acc0 = mfma16(a0[q], wb[q], acc0);
-            if (kChains<T> == 2)
+            if (kChains<T> >= 2)
                 acc1 = mfma16(a1[q], wb[q], acc1);
+            if (kChains<T> == 3)
+                acc2 = mfma16(a2[q], wb[q], acc2);
         }
         // a token's pieces sit in other lanes: through this wave's own LDS block
         f32x4_t* const ub = ucomb + wave * kChains<T> * 64;
         ub[lane] = acc0;
-        if (kChains<T> == 2)
+        if (kChains<T> >= 2)
             ub[64 + lane] = acc1;
+        if (kChains<T> == 3)
+            ub[128 + lane] = acc2;
         asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
         const float* cf = reinterpret_cast<const float*>(ub);
         const int c = c0 + (row >> 2);
@@ -823,6 +919,14 @@ hipError_t launch_decode(int T, const float* R, const float* P, const float* w_n
     case 6: fn = reinterpret_cast<const void*>(&decode_kernel<6>); break;
     case 7: fn = reinterpret_cast<const void*>(&decode_kernel<7>); break;
     case 8: fn = reinterpret_cast<const void*>(&decode_kernel<8>); break;
+    case 9: fn = reinterpret_cast<const void*>(&decode_kernel<9>); break;
+    case 10: fn = reinterpret_cast<const void*>(&decode_kernel<10>); break;
+    case 11: fn = reinterpret_cast<const void*>(&decode_kernel<11>); break;
+    case 12: fn = reinterpret_cast<const void*>(&decode_kernel<12>); break;
+    case 13: fn = reinterpret_cast<const void*>(&decode_kernel<13>); break;
+    case 14: fn = reinterpret_cast<const void*>(&decode_kernel<14>); break;
+    case 15: fn = reinterpret_cast<const void*>(&decode_kernel<15>); break;
+    case 16: fn = reinterpret_cast<const void*>(&decode_kernel<16>); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, dim3(kDecWGs), dim3(kDecThreads), args, 0, stream);

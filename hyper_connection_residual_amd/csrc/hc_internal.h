@@ -30,12 +30,11 @@ constexpr float kEps = 1e-6f;
 // words are 64 bits: payload plus a tag, written once with one store and
 // polled by the consumer.
 // ---------------------------------------------------------------------------
-constexpr int kDecMaxT = 8;
-// Up to this many tokens a read runs as ceil(T / 8) short-window launches over
-// consecutive token ranges; beyond it the wide path (~30 us for 25..128
-// tokens) costs less than streaming the weights once per 8 tokens (~9 us a
-// launch).
-constexpr int kDecSplitMaxT = 24;
+constexpr int kDecMaxT = 16;
+// Up to this many tokens a read runs as ceil(T / 16) short-window launches
+// over consecutive token ranges; beyond it the wide path (~26-31 us for
+// 33..128 tokens) costs less than streaming the weights once per 16 tokens.
+constexpr int kDecSplitMaxT = 32;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;
@@ -47,7 +46,7 @@ constexpr int kDecRedRows = 3;                                   // lo rows each
 constexpr int kDecReducers = (kDecRowsPerXcd + kDecRedRows - 1) / kDecRedRows;  // 14 per XCD
 
 struct DecodeScratch {
-    uint64_t* part;      // [8 xcd][32 wg][40 rows][kDecMaxT]: partial dots (XCD-local)
+    uint64_t* part;      // [8 xcd][32 wg][40 rows][8 or 16 token slots]: partial dots (XCD-local)
     uint64_t* ssq;       // [8 xcd][32 wg][16]: column-slice sums of squares (XCD-local)
     uint64_t* lo;        // [kDecMaxT][kRank]: lo (device-wide)
     uint32_t* gen;       // [kDecWGs]: launches completed by each workgroup

@@ -88,11 +88,11 @@ extern "C" {
  *              (subnormals kept, overflow to +-inf)
  *   stream     hipStream_t to run on (NULL = default stream)
  *
- * T <= 8 runs one launch of the short-window (verify-window) kernel; 9 <= T
- * <= 24 runs ceil(T / 8) of them, on consecutive ranges of at most 8 tokens
- * (a token's read does not depend on the other tokens, and up to 24 tokens
- * streaming the weights once per range costs less than the wide path's fixed
- * cost); larger T runs the wide (prefill) path.  The short-window kernel is
+ * T <= 16 runs one launch of the short-window (verify-window) kernel; 17 <=
+ * T <= 32 runs two, on consecutive ranges of near-equal size (a token's read
+ * does not depend on the other tokens, and up to 32 tokens streaming the
+ * weights once per range costs less than the wide path's fixed cost); larger
+ * T runs the wide (prefill) path.  The short-window kernel is
  * used only where its start-up check passed (see hc_short_window_on);
  * elsewhere every T runs the wide path.  Every valid T is handled; there is no
  * fallback to return.
@@ -133,7 +133,7 @@ HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float
  * "#1370 prefill: opt-in STRATA_HC_UPMIX=1 on CUDA", What it does (BF16 mma
  * with FP32 accumulation), instead of the exact three-piece split of lo.  The
  * norm, the down projection and lo itself are unchanged, and windows of up to
- * 24 tokens (the short-window kernel) give hc_read's result.
+ * 32 tokens (the short-window kernel) give hc_read's result.
  * Its contract is an error bound, not hc_read's 2e-6: every mixed value is
  * within 2^-8 * sum_s |R'[t][s][c]| * sum_j |W_up[s*2560+c][j]| * |lo[t][j]|
  * of the exact read (the bf16 rounding of each lo value), plus hc_read's
@@ -145,7 +145,7 @@ HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, cons
 
 /*
  * hc_short_window_on -- *on = 1 if the current device reads windows of up to
- * 24 tokens with the short-window kernel, 0 if they take the wide path.  The
+ * 32 tokens with the short-window kernel, 0 if they take the wide path.  The
  * kernel's hand-offs need its 256 workgroups resident together and placed on
  * the XCDs the way it expects; once per device (on the first call of any
  * entry point that reads) the library reads 8 tokens through it and through

@@ -78,10 +78,12 @@ def test_ragged_token_counts(T):
     assert_parity(gpu, _oracle(inp), label="T=%d" % T)
 
 
-@pytest.mark.parametrize("T, pending", [(16, True), (24, False), (25, True), (33, True)])
+@pytest.mark.parametrize("T, pending", [(9, True), (12, False), (16, True), (17, True), (24, False), (32, True),
+                                        (33, True)])
 def test_windows_above_eight(T, pending):
-    """9..24 tokens run as ceil(T / 8) short-window launches over consecutive
-    token ranges; 25 is the first count on the wide path.  Full oracle."""
+    """9..16 tokens run as one short-window launch (three MFMA chains, 16
+    token slots per partial row), 17..32 as two on consecutive token ranges;
+    33 is the first count on the wide path.  Full oracle."""
     _case("window of %d tokens, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=5)
     if not pending:
@@ -91,16 +93,16 @@ def test_windows_above_eight(T, pending):
 
 
 def test_split_window_equals_its_ranges():
-    """A 16-token window is two launches of 8: bitwise the reads of its halves."""
-    _case("T=16 against two T=8 reads of its halves")
-    inp = wl.config_inputs(2, T=16, weight_set=9)
+    """A 32-token window is two launches of 16: bitwise the reads of its halves."""
+    _case("T=32 against two T=16 reads of its halves")
+    inp = wl.config_inputs(2, T=32, weight_set=9)
     whole = hip_read(to_device(inp))
-    for lo in (0, 8):
-        half = dataclasses.replace(inp, R=inp.R[lo:lo + 8].copy(), pending=inp.pending[lo:lo + 8].copy())
+    for lo in (0, 16):
+        half = dataclasses.replace(inp, R=inp.R[lo:lo + 16].copy(), pending=inp.pending[lo:lo + 16].copy())
         part = hip_read(to_device(half))
         for a, b in zip(part, whole):
             assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
-                                  (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + 8])
+                                  (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + 16])
 
 
 @pytest.mark.parametrize("T, pending", [(1, True), (5, True), (8, False), (16, True), (300, True), (4097, True)])
@@ -138,7 +140,7 @@ from hyper_connection_residual_amd import binding, workloads as wl
 from oracle import oracle as orc
 from tests.hc_testlib import assert_parity, hip_read, to_device
 assert not binding.hc_short_window_on(), 'the forced check should fail'
-for T in (1, 4, 8, 16):
+for T in (1, 4, 8, 12, 16, 20):
     print('[child] T=%d on the wide path' % T, flush=True)
     inp = wl.config_inputs(2, T=T, weight_set=4)
     gpu = hip_read(to_device(inp))
@@ -152,7 +154,7 @@ def test_forced_check_failure_falls_back_to_the_wide_path():
     """With the bounded waits' limit forced to 0 ticks for the start-up check
     (every wait of the check's read gives up at its first miss, and the
     kernel still ends normally), the check fails, the library logs it, and
-    windows of up to 24 tokens then run the wide path, still at parity.  Run
+    windows of up to 32 tokens then run the wide path, still at parity.  Run
     in a child process, since the check runs once per process."""
     import os
     import subprocess
@@ -202,7 +204,7 @@ def test_bf16_lo_mode_within_its_bound(T, pending):
 
 
 def test_bf16_lo_mode_short_windows_are_exact():
-    """Up to 24 tokens hc_read_bf16_lo is the short-window read: hc_read's bits."""
+    """Up to 32 tokens hc_read_bf16_lo is the short-window read: hc_read's bits."""
     _case("bf16-lo mode at T=8 and T=24 against hc_read")
     for T in (8, 24):
         dev = to_device(wl.config_inputs(2, T=T, weight_set=6))
