@@ -415,41 +415,69 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
                                                   const float* __restrict__ ssq, uint4* __restrict__ lo_tiled)
 {
     constexpr int Q = S / 4;  // splits per stream
-    // four lanes per (token, chunk of 4 rank indices): lane s sums stream s's
-    // Q partials and sums of squares, then the four combine in registers
-    const int idx = (blockIdx.x * 256 + threadIdx.x) >> 2;
-    const int s = threadIdx.x & 3;
+    // Fine splits (short chunks, latency-bound): four lanes per (token, chunk
+    // of 4 rank indices), lane s summing stream s's Q partials, combined in
+    // registers.  Coarse splits (long chunks, bandwidth-bound): one lane sums
+    // all four streams.
+    constexpr int L = S >= 32 ? 4 : 1;
+    const int idx = (blockIdx.x * 256 + threadIdx.x) / L;
     const int t = idx / (kRank / 4);
     const int c4 = idx - t * (kRank / 4);
-    if (t >= Tpad)  // (whole quads: Tpad * 80 quads fill whole waves)
+    if (t >= Tpad)  // (whole lane groups: Tpad * 80 groups fill whole waves)
         return;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T) {
-        float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
+    float lo[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (L == 4) {
+        const int s = threadIdx.x & 3;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < T) {
+            float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int q = 0; q < Q; ++q) {
-            const int sg = Q * s + q;
-            ss += ssq[(size_t)sg * T + t];
-            const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
-            sum[0] += a.x;
-            sum[1] += a.y;
-            sum[2] += a.z;
-            sum[3] += a.w;
+            for (int q = 0; q < Q; ++q) {
+                const int sg = Q * s + q;
+                ss += ssq[(size_t)sg * T + t];
+                const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
+                sum[0] += a.x;
+                sum[1] += a.y;
+                sum[2] += a.z;
+                sum[3] += a.w;
+            }
+            const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = sum[e] * rs;
         }
-        const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+        // (v0 + v1) + (v2 + v3), the same bits in all four lanes
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = v[e] + __shfl_xor(v[e], 1);
+            lo[e] = a + __shfl_xor(a, 2);
+        }
+        if (s != 0)
+            return;
+    } else if (t < T) {
+        float v[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int sg = Q * s + q;
+                ss += ssq[(size_t)sg * T + t];
+                const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
+                sum[0] += a.x;
+                sum[1] += a.y;
+                sum[2] += a.z;
+                sum[3] += a.w;
+            }
+            const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[s][e] = sum[e] * rs;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            v[e] = sum[e] * rs;
+            lo[e] = (v[0][e] + v[1][e]) + (v[2][e] + v[3][e]);
     }
-    // (v0 + v1) + (v2 + v3), the same bits in all four lanes
-    float lo[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float a = v[e] + __shfl_xor(v[e], 1);
-        lo[e] = a + __shfl_xor(a, 2);
-    }
-    if (s != 0)
-        return;
     const int tile = t / kTok, tl = t - tile * kTok;
     const int ks = c4 >> 3, c = c4 & 7;
     lo_tiled[(size_t)(tile * kUpSteps + ks) * kLoTile + 8 * tl + (c ^ swz8(tl))] =
@@ -747,8 +775,9 @@ void launch_down_lo(int Tc, int tiles, const float* Rc, const float* Pc, const f
     else
         hipLaunchKernelGGL((prefill_down<S, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
     const int items = tiles * kTok * (kRank / 4);
-    hipLaunchKernelGGL(prefill_lo<S>, dim3((4 * items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part, ssq,
-                       planes);
+    constexpr int lanes = S >= 32 ? 4 : 1;  // lanes per item (as in prefill_lo)
+    hipLaunchKernelGGL(prefill_lo<S>, dim3((lanes * items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part,
+                       ssq, planes);
 }
 
 // (split, token) slots of the partial array, enough for any chunk of up to

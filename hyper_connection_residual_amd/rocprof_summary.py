@@ -88,7 +88,8 @@ def traffic(fetch_path: str, write_path: str) -> str:
         rd = f_scale * sum(fr) / len(fr)
         wt = w_scale * sum(wr) / len(wr)
         out.append("| %s | %d | %.3f | %.3f |" % (k, len(fr), rd / 1e6, wt / 1e6))
-        if k.startswith("hc::decode_kernel<"):
+        m = re.match(r"hc::decode_kernel<(\d+)>", k)
+        if m and 1 <= int(m.group(1)) <= 8:  # the verify-window sweep's instances
             sweep.append(rd + wt)
     if sweep:
         out += ["", "short-window kernel HBM bytes per launch (sweep average): %d" % round(sum(sweep) / len(sweep)),

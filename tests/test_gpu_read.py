@@ -61,6 +61,15 @@ def test_config2_verify_windows_with_pending(weight_set):
         assert_parity(gpu, _oracle(inp), label="config2 T=%d set=%d" % (T, weight_set))
 
 
+def test_windows_of_9_to_16_every_count():
+    """Every token count of the single-launch range above 8 (three MFMA
+    chains, 16 token slots), with pending.  Full oracle."""
+    for T in range(9, 17):
+        _case("window of %d tokens, pending, weight set 21" % T)
+        inp = wl.config_inputs(2, T=T, weight_set=21)
+        assert_parity(hip_read(to_device(inp)), _oracle(inp), label="T=%d" % T)
+
+
 def test_verify_windows_without_pending():
     for T in range(1, 9):
         _case("config 2 inputs without pending: T=%d" % T)
@@ -383,8 +392,9 @@ def test_graph_replay_matches_eager():
     eager reads on the same stream and synchronisations in between."""
     import torch
     from hyper_connection_residual_amd import binding
-    _case("graph replay: T=1, 5, 8 with pending and T=40 without, 4 replays")
-    inps = [wl.config_inputs(2, T=T, weight_set=30 + T) for T in (1, 5, 8)] + [wl.config_inputs(1, T=40)]
+    _case("graph replay: T=1, 5, 8, 13, 16 and 20 with pending and T=40 without, 4 replays")
+    inps = [wl.config_inputs(2, T=T, weight_set=30 + T % 18) for T in (1, 5, 8, 13, 16, 20)] + \
+        [wl.config_inputs(1, T=40)]
     devs = [to_device(i) for i in inps]
     log = []
 
