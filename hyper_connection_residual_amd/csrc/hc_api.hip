@@ -1,7 +1,7 @@
 // hc_api.hip -- host side of the C ABI declared in include/hc.h: argument
 // checks, per-(device, stream) scratch workspaces, the start-up check of the
-// short-window kernel, and dispatch to the short-window (T <= 32, in launches
-// of up to 16 tokens) and wide (prefill) kernels.
+// short-window kernel, and dispatch to the short-window (T <= 32, one launch)
+// and wide (prefill) kernels.
 #include "hc.h"
 #include "hc_internal.h"
 
@@ -293,7 +293,7 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
         return st;
 
     if (T <= hc::kDecSplitMaxT && short_ok) {
-        // A short window: one launch per range of at most 8 consecutive tokens
+        // A short window: one launch per range of at most kDecMaxT consecutive tokens
         // (ranges of near-equal size).  Every token's read is independent of
         // the others, so the split changes no result.
         const int n = static_cast<int>((T + hc::kDecMaxT - 1) / hc::kDecMaxT);

@@ -1,4 +1,4 @@
-// hc_decode.hip -- the hyper-connection read for short windows (T <= 16 tokens)
+// hc_decode.hip -- the hyper-connection read for short windows (T <= 32 tokens)
 // as ONE kernel launch on gfx950.
 //
 // What it computes is the read of "#315 hc: the multi-token hyper-connection
@@ -38,7 +38,7 @@
 //   three bf16 pieces (hi + mid + lo3 == x), so every product is exact and the
 //   result stays fp32-faithful.  The pieces of all tokens share the MFMA's
 //   rows (row p T + t: piece p of token t), so one chain of MFMAs carries them
-//   when 3 T <= 16, two chains otherwise.
+//   when 3 T <= 16, and 2, 3 or 6 chains for more tokens.
 // * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): 14
 //   of its 32 workgroups each reduce the 32 partials of 3 rows through the
 //   XCD's L2 (hop 1) and publish lo device-wide; every workgroup gathers all of lo
@@ -86,64 +86,81 @@ constexpr int kLoRow = kRank + 8;           // padded LDS row of a lo plane (bf1
 // Every producer writes whole 128-byte lines (16 words), padding unused token
 // slots: a line the XCD's L2 holds only in part is filled from memory when it
 // is read, which costs a memory round trip instead of an L2 hit.
-//   part [8 xcd][32 wg][40 rows][8 tokens]          (two rows per line)
-//   ssq  [8 xcd][32 wg][16]                         (tokens 0..7, then padding)
+//   part [8 xcd][32 wg][40 rows][8 token slots]     (two rows per line), or
+//        [8 xcd][32 wg][40 rows][16 token slots]    (above 8 tokens: one row per line), or
+//        [8 xcd][32 wg][40 rows][32 token slots]    (above 16 tokens: two lines per row)
+//   ssq  [8 xcd][32 wg][16]                         (tokens 0..7, then padding; or tokens 0..15),
+//        or [8 xcd][32 wg][32]                      (above 16 tokens: tokens 0..31)
 //   lo   [8 replica][8 xcd][16 reducer] blocks of 64 words, the first 32 being
-//        [8 tokens][4 rows] (rows 3 u .. 3 u + 2, padding).  Each reducer writes
+//        [8 tokens][4 rows] (rows 3 u .. 3 u + 2, padding; above 8 tokens all
+//        64 are [16 tokens][4 rows]; above 16 tokens the blocks hold 128
+//        words, [32 tokens][4 rows]).  Each reducer writes
 //        one replica per consumer XCD, and the blocks are spread 512 bytes
 //        apart: every line is then read by the 32 workgroups of one XCD,
 //        spread over many memory channels, instead of by all 256 at once.
-constexpr int kSsqLine = 16;
 constexpr int kLoRows = 4;
-constexpr int kLoBlock = 64;
+// Per token count: the ssq words of one workgroup (one line, two above 16
+// tokens), the words of a lo block (2 or 4 lines, 8 above 16 tokens).
+template <int T>
+constexpr int kSsqLine = T <= 16 ? 16 : 32;
+template <int T>
+constexpr int kLoBlock = T <= 16 ? 64 : 128;
 constexpr size_t kPartWords = (size_t)kDecXcds * kDecWgPerXcd * kDecRowsPerXcd * kDecMaxT;
-constexpr size_t kSsqWords = (size_t)kDecXcds * kDecWgPerXcd * kSsqLine;
-constexpr size_t kLoWords = (size_t)kDecXcds * kDecXcds * 16 * kLoBlock;
+constexpr size_t kSsqWords = (size_t)kDecXcds * kDecWgPerXcd * kSsqLine<kDecMaxT>;
+constexpr size_t kLoWords = (size_t)kDecXcds * kDecXcds * 16 * kLoBlock<kDecMaxT>;
 // word index of (token t, reducer row r) of reducer (xs, us) in replica y
+template <int T>
 __host__ __device__ constexpr int lo_word(int y, int xs, int us, int t, int r)
 {
-    return ((y * kDecXcds + xs) * 16 + us) * kLoBlock + t * kLoRows + r;
+    return ((y * kDecXcds + xs) * 16 + us) * kLoBlock<T> + t * kLoRows + r;
 }
 
 // Short-window MFMA blocks put (piece, token) pairs on the 16 A rows: row
 // p T + t holds piece p (0 hi, 1 mid, 2 lo3) of token t.  kChains: MFMA chains
 // per block (1 when all 3 T rows fit; up to 8 tokens 2: pieces 0-1, then
-// piece 2; beyond, 3: one per piece).  kPackRows: the A rows chain 0 carries.
+// piece 2; up to 16, 3: one per piece; beyond, 6: chain 2 p + h carries
+// tokens 16 h .. 16 h + 15 of piece p).  kPackRows: the A rows chain 0 carries.
 template <int T>
-constexpr int kChains = 3 * T <= 16 ? 1 : (T <= 8 ? 2 : 3);
+constexpr int kChains = 3 * T <= 16 ? 1 : (T <= 8 ? 2 : (T <= 16 ? 3 : 6));
 template <int T>
-constexpr int kPackRows = kChains<T> == 1 ? 3 * T : (kChains<T> == 2 ? 2 * T : T);
+constexpr int kPackRows = kChains<T> == 1 ? 3 * T : (kChains<T> == 2 ? 2 * T : (kChains<T> == 3 ? T : 16));
 // First plane row (p T + t) and row count of chain c.
 template <int T>
 __host__ __device__ constexpr int chain_base(int c)
 {
-    return c == 0 ? 0 : (kChains<T> == 3 ? c * T : 2 * T);
+    return kChains<T> == 6 ? (c >> 1) * T + 16 * (c & 1) : (c == 0 ? 0 : (kChains<T> == 3 ? c * T : 2 * T));
 }
 template <int T>
 __host__ __device__ constexpr int chain_rows(int c)
 {
-    return c == 0 ? kPackRows<T> : T;
+    return kChains<T> == 6 ? ((c & 1) ? T - 16 : 16) : (c == 0 ? kPackRows<T> : T);
 }
 // Chains' room in the LDS product blocks (at least 2, as laid out for 1..8 tokens).
 template <int T>
 constexpr int kCombChains = kChains<T> < 2 ? 2 : kChains<T>;
 // Token slots of a partial-dot row in scratch: 8 (two rows per 128-byte
-// line) up to 8 tokens, else 16 (one row per line).
+// line) up to 8 tokens, 16 (one row per line) up to 16, else 32 (two lines).
 template <int T>
-constexpr int kTokSlots = T <= 8 ? 8 : 16;
+constexpr int kTokSlots = T <= 8 ? 8 : (T <= 16 ? 16 : 32);
 
 // LDS map (bytes): both weight tiles, the y planes [3 T][kYRow] bf16, the
 // token sums of squares of the items [T][80] fp32, the down product blocks
-// [6][2 chains][64] f32x4, the lo planes [3 T][kLoRow] bf16, R' of the up
-// tile's rows [T][40] fp32, the up product blocks [3][2 chains][64] f32x4.
-constexpr size_t kOffUTile = 16 * kTileChunks;
-constexpr size_t kOffY = 2 * 16 * kTileChunks;
-template <int T> constexpr size_t kOffSs = kOffY + 2 * 3 * T * kYRow;
+// [6][chains][64] f32x4, the lo planes [3 T][kLoRow] bf16, R' of the up
+// tile's rows [T][40] fp32, the up product blocks [3][chains][64] f32x4.
+// Above 16 tokens, regions never live at once share memory (kShare): the W_up
+// tile lands where the W_down tile was (it is issued after the down MFMAs),
+// the lo planes overwrite the y planes, the up product blocks the down ones.
+template <int T> constexpr bool kShare = T > 16;
+template <int T> constexpr size_t kOffUTile = kShare<T> ? 0 : 16 * kTileChunks;
+template <int T> constexpr size_t kOffY = kOffUTile<T> + 16 * kTileChunks;
+template <int T> constexpr size_t kOffSs = kOffY<T> + 2 * 3 * T * kYRow;
 template <int T> constexpr size_t kOffComb = kOffSs<T> + 4 * T * kStageItems;
-template <int T> constexpr size_t kOffLo = kOffComb<T> + 6 * kCombChains<T> * 64 * 16;
-template <int T> constexpr size_t kOffRp = kOffLo<T> + 2 * 3 * T * kLoRow;
-template <int T> constexpr size_t kOffUComb = kOffRp<T> + 4 * T * kUpRows;
-template <int T> constexpr size_t kLdsBytes = kOffUComb<T> + 3 * kCombChains<T> * 64 * 16;
+template <int T> constexpr size_t kOffLo = kShare<T> ? kOffY<T> : kOffComb<T> + 6 * kCombChains<T> * 64 * 16;
+template <int T>
+constexpr size_t kOffRp = kShare<T> ? kOffComb<T> + 6 * kCombChains<T> * 64 * 16 : kOffLo<T> + 2 * 3 * T * kLoRow;
+template <int T> constexpr size_t kOffUComb = kShare<T> ? kOffComb<T> : kOffRp<T> + 4 * T * kUpRows;
+template <int T>
+constexpr size_t kLdsBytes = kShare<T> ? kOffRp<T> + 4 * T * kUpRows : kOffUComb<T> + 3 * kCombChains<T> * 64 * 16;
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c)
 {
@@ -172,8 +189,8 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
 template <int T>
 __device__ __forceinline__ float packed_at(const float* cf, int w, int p, int t, int n)
 {
-    const int c = kChains<T> == 3 ? p : ((kChains<T> == 2 && p == 2) ? 1 : 0);
-    const int i = kChains<T> == 3 ? t : (c ? t : p * T + t);
+    const int c = kChains<T> == 6 ? 2 * p + (t >> 4) : kChains<T> == 3 ? p : ((kChains<T> == 2 && p == 2) ? 1 : 0);
+    const int i = kChains<T> == 6 ? (t & 15) : kChains<T> == 3 ? t : (c ? t : p * T + t);
     return cf[((w * kChains<T> + c) * 64 + n + 16 * (i >> 2)) * 4 + (i & 3)];
 }
 // The three pieces' products of token t summed: hi + (mid + lo3).
@@ -319,18 +336,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float* __restrict__ out_mixed, uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ out_fp16,
     float* R_commit, long long wait_ticks)
 {
-    static_assert(T >= 1 && T <= kDecMaxT && kDecMaxT == 16, "short-window kernel takes 1..16 tokens");
+    static_assert(T >= 1 && T <= kDecMaxT && kDecMaxT == 32, "short-window kernel takes 1..32 tokens");
     static_assert(kDecRowsPerXcd * kRowChunks == kTileChunks && kUpRows * kRowChunks == kTileChunks,
                   "both tiles are 1600 chunks");
     static_assert(kWidth % kDecDownCols == 0 && kWidth / kDecDownCols == 8, "8 down tiles per stream");
     static_assert(kDecXcds * kDecRowsPerXcd == kRank && kDecWGs * kDecUpCols == kWidth, "cover");
-    static_assert(kStageItems * kDecMaxT <= 3 * kDecThreads && kUpRows * kDecMaxT <= 2 * kDecThreads, "passes");
+    static_assert(kStageItems * kDecMaxT <= 5 * kDecThreads && kUpRows * kDecMaxT <= 3 * kDecThreads, "passes");
     static_assert(kDecReducers <= 16 && kDecRedRows == 3 && kDecWgPerXcd == 32, "reducer layout");
     static_assert(kLdsBytes<T> <= 160 * 1024, "LDS");
     __shared__ __align__(16) uint4 lds[kLdsBytes<T> / 16];
     uint4* const dtile = lds;                                                              // W_down tile
-    uint4* const utile = lds + kOffUTile / 16;                                             // W_up tile
-    uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kOffY / 16);                  // [3 T][kYRow]
+    uint4* const utile = lds + kOffUTile<T> / 16;                                          // W_up tile
+    uint16_t* const ypl = reinterpret_cast<uint16_t*>(lds + kOffY<T> / 16);               // [3 T][kYRow]
     float* const sspart = reinterpret_cast<float*>(lds + kOffSs<T> / 16);                 // [T][80]
     f32x4_t* const comb = reinterpret_cast<f32x4_t*>(lds + kOffComb<T> / 16);             // [6][chains][64]
     uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kOffLo<T> / 16);              // [3 T][kLoRow]
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //     3 u + 2 and their sums of squares.  Polls then hit L2 and see a
     //     producer's store as soon as it lands, instead of each round
     //     fetching the line from memory.
-    uint32_t touched = 0, touched2 = 0;
+    uint32_t touched = 0, touched2 = 0, touched3 = 0, touched4 = 0;
     if (wave == 0 && reducer) {
         const int src = lane & 31, k = lane >> 5;
         const size_t prow = ((size_t)x * kDecWgPerXcd + src) * kDecRowsPerXcd;
@@ -412,20 +429,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             // k 0, 1: the lines of rows 3 u and 3 u + 2 (two rows per line)
             const int row = kDecRedRows * u + 2 * k < kDecRowsPerXcd ? kDecRedRows * u + 2 * k : kDecRowsPerXcd - 1;
             touched = *reinterpret_cast<const uint32_t*>(s.part + (prow + row) * kTokSlots<T>);
-            touched2 = *reinterpret_cast<const uint32_t*>(s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
-        } else {
+            touched2 = *reinterpret_cast<const uint32_t*>(s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine<T>);
+        } else if constexpr (T <= 16) {
             // one row per line: rows 3 u + k, then row 3 u + 2 (k = 0) or the
             // sums of squares (k = 1)
             const int r0 = kDecRedRows * u + k, r2 = kDecRedRows * u + 2;
             touched = *reinterpret_cast<const uint32_t*>(s.part + (prow + r0) * kTokSlots<T>);
             touched2 = *reinterpret_cast<const uint32_t*>(
                 k == 0 ? s.part + (prow + (r2 < kDecRowsPerXcd ? r2 : kDecRowsPerXcd - 1)) * kTokSlots<T>
-                       : s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine);
+                       : s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine<T>);
+        } else {
+            // two lines per row: k = 0 takes both lines of rows 3 u and
+            // 3 u + 1, k = 1 those of row 3 u + 2 and of the sums of squares
+            const int ra = kDecRedRows * u + 2 * k, rb = kDecRedRows * u + 1;
+            const uint64_t* la = s.part + (prow + (ra < kDecRowsPerXcd ? ra : kDecRowsPerXcd - 1)) * kTokSlots<T>;
+            const uint64_t* lb = k == 0 ? s.part + (prow + (rb < kDecRowsPerXcd ? rb : kDecRowsPerXcd - 1)) * kTokSlots<T>
+                                        : s.ssq + ((size_t)x * kDecWgPerXcd + src) * kSsqLine<T>;
+            touched = *reinterpret_cast<const uint32_t*>(la);
+            touched2 = *reinterpret_cast<const uint32_t*>(la + 16);
+            touched3 = *reinterpret_cast<const uint32_t*>(lb);
+            touched4 = *reinterpret_cast<const uint32_t*>(lb + 16);
         }
     }
     // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
     //     and R and pending of those 40 (stream, column) pairs, for the mix
-    constexpr int kUpPasses = (kUpRows * T + kDecThreads - 1) / kDecThreads;  // 1, or 2 above 12 tokens
+    constexpr int kUpPasses = (kUpRows * T + kDecThreads - 1) / kDecThreads;  // 1, 2 above 12 tokens, 3 above 25
     float mr[kUpPasses], mp[kUpPasses];
     auto issue_up = [&]() {
         for (int q = wave; q < kTileInstr; q += 8) {
@@ -470,7 +498,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     }
     wait_all_loads();  // this wave's part of the W_down tile is in LDS
-    asm volatile("" ::"v"(touched), "v"(touched2));
+    asm volatile("" ::"v"(touched), "v"(touched2), "v"(touched3), "v"(touched4));
     wg_barrier();      // B1: y staged, W_down tile complete
     HC_PROBE(1, threadIdx.x == 0);
     pin(seen);
@@ -480,43 +508,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over K
     //     steps 5 (w / 3) .. +4 of 32 columns.  A rows are (piece, token)
     //     pairs in the planes' own order (row p T + t: piece p of token t), so
-    //     one chain of MFMAs carries all three pieces when 3 T <= 16, two
-    //     chains (pieces 0-1, then piece 2) otherwise.
+    //     one chain of MFMAs carries all three pieces when 3 T <= 16, and 2, 3
+    //     or 6 chains carry them for more tokens (kChains).
     if (wave < 6) {
+        constexpr int NC = kChains<T>;
         const int nb = wave % 3, kh = wave / 3;
         const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
         // all operands first (one LDS latency, not five); A rows past the
-        // pieces re-read row 0: they only feed D rows nobody reads
-        const int r0 = chain_base<T>(0) + (m < chain_rows<T>(0) ? m : 0);
-        const int r1 = chain_base<T>(1) + (m < chain_rows<T>(1) ? m : 0);
-        const int r2 = chain_base<T>(2) + (m < chain_rows<T>(2) ? m : 0);
-        uint4 wb[5], a0[5], a1[5], a2[5];
+        // pieces re-read the chain's first row: they only feed D rows nobody reads
+        int ar[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            ar[c] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
+        uint4 wb[5], a[NC][5];
 #pragma unroll
         for (int qq = 0; qq < 5; ++qq) {
             const int q = 5 * kh + qq;
             const int col = 32 * q + 8 * g;
             wb[qq] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
-            a0[qq] = *reinterpret_cast<const uint4*>(&ypl[r0 * kYRow + col]);
-            if (kChains<T> >= 2)
-                a1[qq] = *reinterpret_cast<const uint4*>(&ypl[r1 * kYRow + col]);
-            if (kChains<T> == 3)
-                a2[qq] = *reinterpret_cast<const uint4*>(&ypl[r2 * kYRow + col]);
-        }
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
-        for (int qq = 0; qq < 5; ++qq) {
-            acc0 = mfma16(a0[qq], wb[qq], acc0);
-            if (kChains<T> >= 2)
-                acc1 = mfma16(a1[qq], wb[qq], acc1);
-            if (kChains<T> == 3)
-                acc2 = mfma16(a2[qq], wb[qq], acc2);
+            for (int c = 0; c < NC; ++c)
+                a[c][qq] = *reinterpret_cast<const uint4*>(&ypl[ar[c] * kYRow + col]);
         }
-        comb[(wave * kChains<T>) * 64 + lane] = acc0;
-        if (kChains<T> >= 2)
-            comb[(wave * kChains<T> + 1) * 64 + lane] = acc1;
-        if (kChains<T> == 3)
-            comb[(wave * kChains<T> + 2) * 64 + lane] = acc2;
-    } else if (wave == 6) {
+        f32x4_t acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int qq = 0; qq < 5; ++qq)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[c] = mfma16(a[c][qq], wb[qq], acc[c]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            comb[(wave * NC + c) * 64 + lane] = acc[c];
+    } else if (wave == 6 || (T > 16 && wave == 7)) {
         // (7') meanwhile, the slice's sum of squares per token: lane 8 t + p
         //      sums 10 of token t's 80 item sums, then the 8 lanes combine theirs
         if constexpr (T <= 8) {
@@ -529,12 +555,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             ss = sum8(ss);
             if (p < 2)  // words 0..7: tokens (0 past T); words 8..15: padding -- one whole line
-                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + 8 * p + tt],
+                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine<T> + 8 * p + tt],
                             tag_f32(p == 0 ? ss : 0.f, xcd_tag(gen, rot)));
         } else {
             // lane 4 t + p sums 20 of token t's 80 item sums, then the 4
-            // lanes combine theirs; words 0..15: tokens (0 past T)
-            const int tt = lane >> 2, p = lane & 3;
+            // lanes combine theirs; words 0..15: tokens (0 past T); above 16
+            // tokens waves 6 and 7 share the work (lane 4 t + p of their 128),
+            // words 0..31 (two lines, one per wave)
+            const int l = threadIdx.x - 6 * 64, tt = l >> 2, p = l & 3;
             float ss = 0.f;
             if (tt < T) {
 #pragma unroll
@@ -543,7 +571,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             ss = sum4(ss);
             if (p == 0)
-                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine + tt], tag_f32(ss, xcd_tag(gen, rot)));
+                st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine<T> + tt], tag_f32(ss, xcd_tag(gen, rot)));
         }
     }
     HC_PROBE(2, threadIdx.x == 0);
@@ -553,7 +581,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         // (8) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g, into
         //     the XCD's L2: per K half hi + (mid + lo3), then the two halves
         //     (all 8 token slots, whole lines; slots >= T hold 0)
-        //     (above 8 tokens each lane also takes token t + 8: 16 slots)
+        //     (above 8 tokens each lane also takes tokens t + 8, t + 16, ...:
+        //     16 or 32 slots)
         const float* cf = reinterpret_cast<const float*>(comb);
         const int nb = wave % 3, t = 4 * (wave / 3) + g;
         const int row = 16 * nb + n;
@@ -585,7 +614,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         const long long t0 = wall_clock64();
         const int src = lane & 15, k = lane >> 4;
         const int pa0 = (x * kDecWgPerXcd + src) * kDecRowsPerXcd, pb0 = pa0 + 16 * kDecRowsPerXcd;
-        const int sa0 = (x * kDecWgPerXcd + src) * kSsqLine, sb0 = sa0 + 16 * kSsqLine;
+        const int sa0 = (x * kDecWgPerXcd + src) * kSsqLine<T>, sb0 = sa0 + 16 * kSsqLine<T>;
         // lo of (stream pair sums) -> (s0 + s1) + (s2 + s3), the same in all 16 lanes
         auto combine = [](float pa, float pb, float qa, float qb) {
             const float rsa = rsqrtf(sum8(qa) * (1.0f / (float)kWidth) + kEps);
@@ -649,7 +678,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
             for (int y = 0; y < kDecXcds; ++y)
                 if (src < 8)
-                    st_word(&s.lo[lo_word(y, x, u, src, k)], word);
+                    st_word(&s.lo[lo_word<T>(y, x, u, src, k)], word);
         } else {
             // token pairs: lane group k takes pairs k + 4 q (q < NQ: tokens
             // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows
@@ -707,21 +736,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                                                __uint_as_float(h ? wb_[rr][q].z : wb_[rr][q].x),
                                                __uint_as_float(h ? qa_[q].z : qa_[q].x),
                                                __uint_as_float(h ? qb_[q].z : qb_[q].x));
-            // lane src < 8 NQ of group k writes row (src / 2) % 4 (row 3:
-            // padding), token 2 k + src % 2 + 8 (src / 8)
-            const int rr = (src >> 1) & 3, h = src & 1, q = src >> 3, tok = 2 * k + h + 8 * q;
-            float mine = 0.f;
+            // lane src of group k writes row (src / 2) % 4 (row 3: padding),
+            // token 2 k + src % 2 + 8 q for q = src / 8 (+ 2 w: with 4 pair
+            // groups each lane writes two words)
+            constexpr int NW = NQ > 2 ? 2 : 1;
 #pragma unroll
-            for (int qq = 0; qq < NQ; ++qq)
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const int rr = (src >> 1) & 3, h = src & 1, q = (src >> 3) + 2 * w2, tok = 2 * k + h + 8 * q;
+                float mine = 0.f;
 #pragma unroll
-                for (int r3 = 0; r3 < kDecRedRows; ++r3)
-                    mine = (qq == q && r3 == rr) ? (h ? lo[r3][qq][1] : lo[r3][qq][0]) : mine;
-            const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
-            const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
+                for (int qq = 0; qq < NQ; ++qq)
 #pragma unroll
-            for (int y = 0; y < kDecXcds; ++y)
-                if (src < 8 * NQ)
-                    st_word(&s.lo[lo_word(y, x, u, tok, rr)], word);
+                    for (int r3 = 0; r3 < kDecRedRows; ++r3)
+                        mine = (qq == q && r3 == rr) ? (h ? lo[r3][qq][1] : lo[r3][qq][0]) : mine;
+                const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
+                const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
+#pragma unroll
+                for (int y = 0; y < kDecXcds; ++y)
+                    if (q < NQ)
+                        st_word(&s.lo[lo_word<T>(y, x, u, tok, rr)], word);
+            }
         }
         HC_PROBE(13, lane == 0);
     }
@@ -744,7 +778,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const int sl = lane + 64 * k < NSL ? lane + 64 * k : 0;  // (past the end: re-read slot 0)
             const int pair = sl & 1, rest = sl >> 1;
             const int tt = rest % T, us = rest / T;  // us: reducer 0 .. 13
-            widx[k] = lo_word(x, wave, us, tt, 2 * pair);
+            widx[k] = lo_word<T>(x, wave, us, tt, 2 * pair);
         }
         [[maybe_unused]] int rounds = 0;
         while (true) {
@@ -817,52 +851,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     }
 
-    if (wave < 3) {
-        // (11) up projection: wave w < 3 takes tile rows 16 w .. +15 (slot n =
-        //      4 column + stream; block 2: rows 32..39, its upper 8 slots
-        //      repeat them), all 10 K steps, A rows packed as in the down
-        //      projection; gated = up (identity epilogue); then the mix of the
-        //      4 streams of a column
-        const int row = wave < 2 ? 16 * wave + n : 32 + (n & 7);
+    constexpr bool kSplitUp = kChains<T> == 6;  // above 16 tokens: one token half per wave
+    if (wave < (kSplitUp ? 6 : 3)) {
+        // (11) up projection: wave w takes tile rows 16 rb .. +15, rb = w % 3
+        //      (slot n = 4 column + stream; block 2: rows 32..39, its upper 8
+        //      slots repeat them), all 10 K steps, A rows packed as in the down
+        //      projection (above 16 tokens: waves 0-2 the chains of tokens
+        //      0..15, waves 3-5 those of tokens 16..); gated = up (identity
+        //      epilogue); then the mix of the 4 streams of a column
+        constexpr int UC = kSplitUp ? 3 : kChains<T>;  // chains per wave
+        const int rb = wave % 3, th = kSplitUp ? wave / 3 : 0;
+        const int row = rb < 2 ? 16 * rb + n : 32 + (n & 7);
         const int st = n & 3;
-        const int r0 = chain_base<T>(0) + (m < chain_rows<T>(0) ? m : 0);
-        const int r1 = chain_base<T>(1) + (m < chain_rows<T>(1) ? m : 0);
-        const int r2 = chain_base<T>(2) + (m < chain_rows<T>(2) ? m : 0);
-        uint4 wb[10], a0[10], a1[10], a2[10];
+        int ar[UC];
+#pragma unroll
+        for (int j = 0; j < UC; ++j) {
+            const int c = kSplitUp ? 2 * j + th : j;
+            ar[j] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
+        }
+        uint4 wb[10], a[UC][10];
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             const int jc = 32 * q + 8 * g;
             wb[q] = utile[tile_pos<kRowChunks>(row, 4 * q + g)];
-            a0[q] = *reinterpret_cast<const uint4*>(&lpl[r0 * kLoRow + jc]);
-            if (kChains<T> >= 2)
-                a1[q] = *reinterpret_cast<const uint4*>(&lpl[r1 * kLoRow + jc]);
-            if (kChains<T> == 3)
-                a2[q] = *reinterpret_cast<const uint4*>(&lpl[r2 * kLoRow + jc]);
-        }
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
 #pragma unroll
-        for (int q = 0; q < 10; ++q) {
-            acc0 = mfma16(a0[q], wb[q], acc0);
-            if (kChains<T> >= 2)
-                acc1 = mfma16(a1[q], wb[q], acc1);
-            if (kChains<T> == 3)
-                acc2 = mfma16(a2[q], wb[q], acc2);
+            for (int j = 0; j < UC; ++j)
+                a[j][q] = *reinterpret_cast<const uint4*>(&lpl[ar[j] * kLoRow + jc]);
         }
+        f32x4_t acc[UC];
+#pragma unroll
+        for (int j = 0; j < UC; ++j)
+            acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 10; ++q)
+#pragma unroll
+            for (int j = 0; j < UC; ++j)
+                acc[j] = mfma16(a[j][q], wb[q], acc[j]);
         // a token's pieces sit in other lanes: through this wave's own LDS block
-        f32x4_t* const ub = ucomb + wave * kChains<T> * 64;
-        ub[lane] = acc0;
-        if (kChains<T> >= 2)
-            ub[64 + lane] = acc1;
-        if (kChains<T> == 3)
-            ub[128 + lane] = acc2;
+        f32x4_t* const ub = ucomb + wave * UC * 64;
+#pragma unroll
+        for (int j = 0; j < UC; ++j)
+            ub[64 * j + lane] = acc[j];
         asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
         const float* cf = reinterpret_cast<const float*>(ub);
         const int c = c0 + (row >> 2);
-        const bool owner = st == 0 && (wave < 2 || n < 8);  // (block 2's upper slots are copies)
+        const bool owner = st == 0 && (rb < 2 || n < 8);  // (block 2's upper slots are copies)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int tt = 4 * g + e;
-            const float up = tt < T ? piece_sum<T>(cf, 0, tt, n) : 0.f;
+            const int i16 = 4 * g + e, tt = 16 * th + i16;
+            // block j holds piece j of tokens 16 th + i16 (row i16 of the block)
+            auto at = [&](int j) { return cf[(64 * j + n + 16 * (i16 >> 2)) * 4 + (i16 & 3)]; };
+            const float up = tt < T ? (kSplitUp ? at(0) + (at(1) + at(2)) : piece_sum<T>(cf, 0, tt, n)) : 0.f;
             const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
             const float mixed = sum4(up * rp);  // (s0 + s1) + (s2 + s3)
             if (owner && tt < T) {
@@ -896,9 +935,16 @@ void decode_scratch_carve(void* base, DecodeScratch* s)
 
 hipError_t decode_resident_blocks(int* blocks_per_cu)
 {
-    // the largest-LDS instance bounds residency for every T
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void*>(&decode_kernel<kDecMaxT>), kDecThreads, 0);
+    // the largest-LDS instances (16 tokens without shared regions, 32 with)
+    // bound residency for every T
+    int a = 0, c = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &a, reinterpret_cast<const void*>(&decode_kernel<16>), kDecThreads, 0);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &c, reinterpret_cast<const void*>(&decode_kernel<kDecMaxT>), kDecThreads, 0);
+    *blocks_per_cu = a < c ? a : c;
+    return e;
 }
 
 hipError_t launch_decode(int T, const float* R, const float* P, const float* w_norm,
@@ -927,6 +973,22 @@ hipError_t launch_decode(int T, const float* R, const float* P, const float* w_n
     case 14: fn = reinterpret_cast<const void*>(&decode_kernel<14>); break;
     case 15: fn = reinterpret_cast<const void*>(&decode_kernel<15>); break;
     case 16: fn = reinterpret_cast<const void*>(&decode_kernel<16>); break;
+    case 17: fn = reinterpret_cast<const void*>(&decode_kernel<17>); break;
+    case 18: fn = reinterpret_cast<const void*>(&decode_kernel<18>); break;
+    case 19: fn = reinterpret_cast<const void*>(&decode_kernel<19>); break;
+    case 20: fn = reinterpret_cast<const void*>(&decode_kernel<20>); break;
+    case 21: fn = reinterpret_cast<const void*>(&decode_kernel<21>); break;
+    case 22: fn = reinterpret_cast<const void*>(&decode_kernel<22>); break;
+    case 23: fn = reinterpret_cast<const void*>(&decode_kernel<23>); break;
+    case 24: fn = reinterpret_cast<const void*>(&decode_kernel<24>); break;
+    case 25: fn = reinterpret_cast<const void*>(&decode_kernel<25>); break;
+    case 26: fn = reinterpret_cast<const void*>(&decode_kernel<26>); break;
+    case 27: fn = reinterpret_cast<const void*>(&decode_kernel<27>); break;
+    case 28: fn = reinterpret_cast<const void*>(&decode_kernel<28>); break;
+    case 29: fn = reinterpret_cast<const void*>(&decode_kernel<29>); break;
+    case 30: fn = reinterpret_cast<const void*>(&decode_kernel<30>); break;
+    case 31: fn = reinterpret_cast<const void*>(&decode_kernel<31>); break;
+    case 32: fn = reinterpret_cast<const void*>(&decode_kernel<32>); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, dim3(kDecWGs), dim3(kDecThreads), args, 0, stream);

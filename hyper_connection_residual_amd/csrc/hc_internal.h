@@ -30,10 +30,10 @@ constexpr float kEps = 1e-6f;
 // words are 64 bits: payload plus a tag, written once with one store and
 // polled by the consumer.
 // ---------------------------------------------------------------------------
-constexpr int kDecMaxT = 16;
-// Up to this many tokens a read runs as ceil(T / 16) short-window launches
-// over consecutive token ranges; beyond it the wide path (~26-31 us for
-// 33..128 tokens) costs less than streaming the weights once per 16 tokens.
+constexpr int kDecMaxT = 32;
+// Up to this many tokens a read runs as ceil(T / kDecMaxT) short-window
+// launches over consecutive token ranges (one launch while T <= kDecMaxT);
+// beyond it the wide path costs less than streaming the weights once per range.
 constexpr int kDecSplitMaxT = 32;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;

@@ -88,10 +88,7 @@ extern "C" {
  *              (subnormals kept, overflow to +-inf)
  *   stream     hipStream_t to run on (NULL = default stream)
  *
- * T <= 16 runs one launch of the short-window (verify-window) kernel; 17 <=
- * T <= 32 runs two, on consecutive ranges of near-equal size (a token's read
- * does not depend on the other tokens, and up to 32 tokens streaming the
- * weights once per range costs less than the wide path's fixed cost); larger
+ * T <= 32 runs one launch of the short-window (verify-window) kernel; larger
  * T runs the wide (prefill) path.  The short-window kernel is
  * used only where its start-up check passed (see hc_short_window_on);
  * elsewhere every T runs the wide path.  Every valid T is handled; there is no

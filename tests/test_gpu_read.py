@@ -70,6 +70,15 @@ def test_windows_of_9_to_16_every_count():
         assert_parity(hip_read(to_device(inp)), _oracle(inp), label="T=%d" % T)
 
 
+def test_windows_of_17_to_32_every_count():
+    """Every token count of the six-chain range (32 token slots, LDS regions
+    shared between phases), with pending.  Full oracle."""
+    for T in range(17, 33):
+        _case("window of %d tokens, pending, weight set 22" % T)
+        inp = wl.config_inputs(2, T=T, weight_set=22)
+        assert_parity(hip_read(to_device(inp)), _oracle(inp), label="T=%d" % T)
+
+
 def test_verify_windows_without_pending():
     for T in range(1, 9):
         _case("config 2 inputs without pending: T=%d" % T)
@@ -90,9 +99,9 @@ def test_ragged_token_counts(T):
 @pytest.mark.parametrize("T, pending", [(9, True), (12, False), (16, True), (17, True), (24, False), (32, True),
                                         (33, True)])
 def test_windows_above_eight(T, pending):
-    """9..16 tokens run as one short-window launch (three MFMA chains, 16
-    token slots per partial row), 17..32 as two on consecutive token ranges;
-    33 is the first count on the wide path.  Full oracle."""
+    """9..16 tokens run as one short-window launch with three MFMA chains and
+    16 token slots per partial row, 17..32 with six chains and 32 slots; 33
+    is the first count on the wide path.  Full oracle."""
     _case("window of %d tokens, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=5)
     if not pending:
@@ -101,25 +110,29 @@ def test_windows_above_eight(T, pending):
     assert_parity(gpu, _oracle(inp), label="T=%d pending=%s" % (T, pending))
 
 
-def test_split_window_equals_its_ranges():
-    """A 32-token window is two launches of 16: bitwise the reads of its halves."""
-    _case("T=32 against two T=16 reads of its halves")
-    inp = wl.config_inputs(2, T=32, weight_set=9)
+@pytest.mark.parametrize("T, half", [(32, 16), (20, 10)])
+def test_window_equals_its_halves(T, half):
+    """Above 8 tokens a token's arithmetic does not depend on the window: the
+    six-chain kernel (17..32 tokens) gives every token the bits that the
+    three-chain kernel gives it in a window of half the size."""
+    _case("T=%d against two T=%d reads of its halves" % (T, half))
+    inp = wl.config_inputs(2, T=T, weight_set=9)
     whole = hip_read(to_device(inp))
-    for lo in (0, 16):
-        half = dataclasses.replace(inp, R=inp.R[lo:lo + 16].copy(), pending=inp.pending[lo:lo + 16].copy())
-        part = hip_read(to_device(half))
+    for lo in (0, half):
+        part_in = dataclasses.replace(inp, R=inp.R[lo:lo + half].copy(), pending=inp.pending[lo:lo + half].copy())
+        part = hip_read(to_device(part_in))
         for a, b in zip(part, whole):
             assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
-                                  (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + 16])
+                                  (b.view(np.uint32) if b.dtype == np.float32 else b)[lo:lo + half])
 
 
-@pytest.mark.parametrize("T, pending", [(1, True), (5, True), (8, False), (16, True), (300, True), (4097, True)])
+@pytest.mark.parametrize("T, pending", [(1, True), (5, True), (8, False), (16, True), (24, True), (300, True),
+                                        (4097, True)])
 def test_commit_writes_the_pending_update(T, pending):
     """hc_read_commit: the outputs are hc_read's, bit for bit, and R then holds
     the oracle's committed residual fl32(R + pending), bit for bit (untouched
-    without a pending write).  Covers the short-window kernel, the split
-    window, and the wide path over two chunks."""
+    without a pending write).  Covers the short-window kernel at 1, 2, 3 and 6
+    MFMA chains, and the wide path over two chunks."""
     _case("commit: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=2) if T <= 24 else wl.config_inputs(5, T=T, seed=T)
     if not pending:
