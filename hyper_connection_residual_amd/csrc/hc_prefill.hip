@@ -159,9 +159,9 @@ constexpr int kLoTile = kTok * 8;              // fp32 lo of one (token tile, K 
 // matrix waves and one producer): the vector work of the producers overlaps
 // the matrix cores instead of adding to them, and two matrix waves per SIMD
 // keep its matrix core issuing.
-//  * matrix waves 0-7: wave m computes all 320 rows for tokens 16 m .. +15:
-//    MFMA A = W_down rows (20 blocks of 16), B = the y panels of its token
-//    block; it reads LDS and issues MFMAs only.
+//  * matrix waves 0-7: wave m computes rows 160 (m % 2) .. +159 for tokens
+//    32 (m / 2) .. +31: MFMA A = W_down rows (10 blocks of 16), B = the y
+//    panels of its two token blocks; it reads LDS and issues MFMAs only.
 //  * producer waves 8-11: issue every load (the W_down panel of a step one step
 //    ahead, raw R and pending three steps ahead, the split's w_norm once) and
 //    turn the raw activations of the next step into y = R' * w_norm, split
@@ -329,23 +329,32 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
     }
 
     // ============================= matrix =============================
+    // wave m computes rows 160 (m % 2) .. +159 for tokens 32 (m / 2) .. +31:
+    // per K step it reads 10 KB of W_down and 6 KB of y from LDS (a 16-token x
+    // 320-row tile would read 23 KB), for the same 60 MFMAs
     const int m = wave;
+    const int rh = m & 1, tq = m >> 1;
     const int n = lane & 15, g = lane >> 4;
-    f32x4_t acc[20];
+    f32x4_t acc[10][2];
 #pragma unroll
-    for (int jb = 0; jb < 20; ++jb)
-        acc[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // operands: W_down row block jb = this lane's slot in block 0 plus 1 KB per
-    // block; y of token 16 m + n, chunk g, panel p
-    const uint32_t aoff = 16 * panel_slot(n, g);
-    const uint32_t yoff = 16 * panel_slot(16 * m + n, g);
+    for (int jb = 0; jb < 10; ++jb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+            acc[jb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // operands: W_down row block 10 rh + jb = this lane's slot in block 0 plus
+    // 1 KB per block; y of token 32 tq + 16 tb + n, chunk g, panel p (a 16-row
+    // block further is 1 KB further: the panel swizzle repeats every 8 rows)
+    const uint32_t aoff = 16 * panel_slot(n, g) + 10240 * rh;
+    const uint32_t yoff = 16 * panel_slot(32 * tq + n, g);
     auto compute = [&](int ks) {
         const uint32_t wb = lds0 + 16 * (kWOff + (ks & 1) * kDnWChunks) + aoff;
-        const uint32_t yb = lds0 + 16 * (kYOff + (ks & 1) * kDnYChunks);
-        u32x4 y[3];
+        const uint32_t yb = lds0 + 16 * (kYOff + (ks & 1) * kDnYChunks) + yoff;
+        u32x4 y[3][2];
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-            y[p] = ds_read16(yb + yoff + 16 * kDnTok * 4 * p);
+        for (int p = 0; p < 3; ++p) {
+            y[p][0] = ds_read16(yb + 16 * kDnTok * 4 * p);
+            y[p][1] = ds_read16(yb + 16 * kDnTok * 4 * p + 1024);
+        }
         u32x4 wa[5];
         wa[0] = ds_read16_off<0>(wb);
         wa[1] = ds_read16_off<1024>(wb);
@@ -354,15 +363,17 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
         wa[4] = ds_read16_off<4096>(wb);
         asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory");
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-            asm volatile("" : "+v"(y[p]));
-        // 4 groups of 5 row blocks: the next group's operands are read while
-        // this group's 15 MFMAs run
+        for (int p = 0; p < 3; ++p) {
+            asm volatile("" : "+v"(y[p][0]));
+            asm volatile("" : "+v"(y[p][1]));
+        }
+        // 2 groups of 5 row blocks: the second group's operands are read
+        // while the first group's 30 MFMAs run
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
+        for (int grp = 0; grp < 2; ++grp) {
             u32x4 wn[5];
-            if (grp < 3) {
-                const uint32_t wg = wb + 5120 * (grp + 1);
+            if (grp == 0) {
+                const uint32_t wg = wb + 5120;
                 wn[0] = ds_read16_off<0>(wg);
                 wn[1] = ds_read16_off<1024>(wg);
                 wn[2] = ds_read16_off<2048>(wg);
@@ -378,9 +389,11 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
 #pragma unroll
             for (int p = 2; p >= 0; --p)
 #pragma unroll
-                for (int jb = 0; jb < 5; ++jb)
-                    acc[5 * grp + jb] = mfma16(wa[jb], y[p], acc[5 * grp + jb]);
-            if (grp < 3) {
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int jb = 0; jb < 5; ++jb)
+                        acc[5 * grp + jb][tb] = mfma16(wa[jb], y[p][tb], acc[5 * grp + jb][tb]);
+            if (grp == 0) {
 #pragma unroll
                 for (int jb = 0; jb < 5; ++jb)
                     wa[jb] = wn[jb];
@@ -394,13 +407,17 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
         compute(j);
         ring_barrier<0>();  // B(j + 2)
     }
-    // partials: lane holds token t0 + 16 m + n, rows 16 jb + 4 g .. +3
-    const int t = t0 + 16 * m + n;
-    if (t < T) {
-        float* dst = part + ((size_t)sig * T + t) * kRank + 4 * g;
+    // partials: lane holds tokens t0 + 32 tq + 16 tb + n, rows 160 rh + 16 jb
+    // + 4 g .. +3
 #pragma unroll
-        for (int jb = 0; jb < 20; ++jb)
-            *reinterpret_cast<f32x4_t*>(dst + 16 * jb) = acc[jb];
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = t0 + 32 * tq + 16 * tb + n;
+        if (t < T) {
+            float* dst = part + ((size_t)sig * T + t) * kRank + 160 * rh + 4 * g;
+#pragma unroll
+            for (int jb = 0; jb < 10; ++jb)
+                *reinterpret_cast<f32x4_t*>(dst + 16 * jb) = acc[jb][tb];
+        }
     }
 }
 
