@@ -512,13 +512,24 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
 // LDS stage (24 KB): W_up panel (256 rows: row 64 s + j = W_up row
 // s * 2560 + c0 + j, 16 KB), then the tile's lo block of the step (8 KB).
 // Three stages, loaded two steps ahead.
+// Chunks of at most 4 token tiles use tiles of 16 columns instead (CB = 1
+// column block instead of 4): 160 workgroups per token tile, each streaming
+// a quarter of the W_up panel, so a short read loads W_up over most of the
+// chip instead of 40 CUs.
 // ---------------------------------------------------------------------------
-constexpr int kUpWChunks = 4 * kUpCols * 4;      // 1024
-constexpr int kUpStage = kUpWChunks + kLoTile;   // 1536 chunks
 constexpr int kUpSlots = 3;
-constexpr int kUpLoads = (kUpWChunks + kLoTile) / 64 / 4;  // wave instructions per stage and wave (6)
 
-template <bool HAS_P, bool BF16_LO>
+// Calls f(std::integral_constant<int, K>) for K = K0 .. K0 + N - 1.
+template <int K0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (N > 0) {
+        f(std::integral_constant<int, K0>{});
+        static_for<K0 + 1, N - 1>(f);
+    }
+}
+
+template <bool HAS_P, bool BF16_LO, int CB>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* R,
@@ -528,13 +539,20 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                                                         uint16_t* __restrict__ out_fp16,
                                                         float* R_commit)
 {
+    static_assert(CB == 4 || CB == 1, "column blocks");
+    constexpr int kCols = 16 * CB;                      // output columns of the tile
+    constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (5 or 20)
+    constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 1024 or 256 chunks
+    constexpr int kUpStage = kUpWChunks + kLoTile;      // 1536 or 768 chunks
+    constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (6 or 3)
+    constexpr int NB = 2 * CB;                          // panel blocks of two streams
     __shared__ __align__(16) uint4 lds[kUpSlots * kUpStage];
 
     const int b = blockIdx.x;
     const int x = b & 7, q = b >> 3;
-    const int tile = q / kGroupsPerXcd;
-    const int cg = x + 8 * (q - tile * kGroupsPerXcd);
-    const int t0 = tile * kTok, c0 = cg * kUpCols;
+    const int tile = q / kGpx;
+    const int cg = x + 8 * (q - tile * kGpx);
+    const int t0 = tile * kTok, c0 = cg * kCols;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -544,26 +562,26 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
     // instruction i (0..7) copies 1 KB of the lo block.  Wave w issues W_up
     // i = w + 4 k (k < 4) and lo i = w, w + 4.
     const int wchunk = (lane & 3) ^ ((lane >> 3) & 3);
-    const uint16_t* wu_lane[4];
+    const uint16_t* wu_lane[CB];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int prow = 16 * (wave + 4 * k) + (lane >> 2);  // panel row = 64 s + j
-        wu_lane[k] = W_up + (size_t)((prow >> 6) * kWidth + c0 + (prow & 63)) * kRank + 8 * wchunk;
+    for (int k = 0; k < CB; ++k) {
+        const int prow = 16 * (wave + 4 * k) + (lane >> 2);  // panel row = kCols s + j
+        wu_lane[k] = W_up + (size_t)((prow / kCols) * kWidth + c0 + (prow % kCols)) * kRank + 8 * wchunk;
     }
     const uint4* lo_lane = lo_tiled + (size_t)tile * kUpSteps * kLoTile + lane;
     auto issue = [&](int ks, int slot) {
         uint4* sb = lds + slot * kUpStage;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < CB; ++k)
             dma16(wu_lane[k] + kKs * ks, sb + 64 * (wave + 4 * k));
 #pragma unroll
         for (int k = 0; k < 2; ++k)
             dma16(lo_lane + (size_t)ks * kLoTile + 64 * (wave + 4 * k), sb + kUpWChunks + 64 * (wave + 4 * k));
     };
 
-    f32x4_t acc[4][4];  // [column block][stream]
+    f32x4_t acc[CB][4];  // [column block][stream]
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             acc[cb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -581,17 +599,10 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         u32x4 lv[2];
         lv[0] = ds_read16(sb + lo_a);
         lv[1] = ds_read16(sb + lo_b);
-        u32x4 wa[8];
+        u32x4 wa[NB];
         const uint32_t wb = sb + aoff;
-        wa[0] = ds_read16_off<0>(wb);
-        wa[1] = ds_read16_off<1024>(wb);
-        wa[2] = ds_read16_off<2048>(wb);
-        wa[3] = ds_read16_off<3072>(wb);
-        wa[4] = ds_read16_off<4096>(wb);
-        wa[5] = ds_read16_off<5120>(wb);
-        wa[6] = ds_read16_off<6144>(wb);
-        wa[7] = ds_read16_off<7168>(wb);
-        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+        static_for<0, NB>([&](auto kc) { constexpr int k = decltype(kc)::value; wa[k] = ds_read16_off<1024 * k>(wb); });
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NB) : "memory");
         asm volatile("" : "+v"(lv[0]), "+v"(lv[1]));
         uint32_t hi[8], mi[8] = {}, l3[8] = {};
 #pragma unroll
@@ -607,45 +618,38 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         y[2] = u32x4{l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16)};
         // streams 0-1 (column blocks 0..3) then streams 2-3: the second half's
         // W_up operands are read while the first half's 24 MFMAs run
-        u32x4 wn[8];
-        wn[0] = ds_read16_off<8192>(wb);
-        wn[1] = ds_read16_off<9216>(wb);
-        wn[2] = ds_read16_off<10240>(wb);
-        wn[3] = ds_read16_off<11264>(wb);
-        wn[4] = ds_read16_off<12288>(wb);
-        wn[5] = ds_read16_off<13312>(wb);
-        wn[6] = ds_read16_off<14336>(wb);
-        wn[7] = ds_read16_off<15360>(wb);
-        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+        u32x4 wn[NB];
+        static_for<0, NB>([&](auto kc) { constexpr int k = decltype(kc)::value; wn[k] = ds_read16_off<1024 * (NB + k)>(wb); });
+        asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(NB) : "memory");
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < NB; ++k)
             asm volatile("" : "+v"(wa[k]));
-        // panel block index k = 4 s + cb
+        // panel block index k = CB s + cb
 #pragma unroll
         for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                acc[k & 3][k >> 2] = mfma16(wa[k], y[p], acc[k & 3][k >> 2]);
+            for (int k = 0; k < NB; ++k)
+                acc[k % CB][k / CB] = mfma16(wa[k], y[p], acc[k % CB][k / CB]);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < NB; ++k)
             asm volatile("" : "+v"(wn[k]));
 #pragma unroll
         for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                acc[k & 3][2 + (k >> 2)] = mfma16(wn[k], y[p], acc[k & 3][2 + (k >> 2)]);
+            for (int k = 0; k < NB; ++k)
+                acc[k % CB][2 + k / CB] = mfma16(wn[k], y[p], acc[k % CB][2 + k / CB]);
     };
 
     // The epilogue's R: this lane's token, columns c0 + 16 cb + 4 g .. +3 of
     // every stream (tokens past T re-read token T - 1 and store nothing).
     // Its 16 loads are issued two steps before the end of the K loop, after
     // the last stage's loads, and are counted in the waits that follow.
-    constexpr int kRLoads = 16;
+    constexpr int kRLoads = 4 * CB;
     const int t = t0 + lrow;
     const int tr = t < T ? t : T - 1;
     const float* rrow = R + (size_t)tr * kD + c0 + 4 * g;
-    float4 rv[4][4];  // [column block][stream]
+    float4 rv[CB][4];  // [column block][stream]
 
     // Step ks: stage ks + 2 is issued (the wait at the end of the step leaves
     // exactly those loads in flight); the matrix cores run step ks.
@@ -670,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         gf32x4* rl = (gf32x4*)rrow;  // (an address-space cast: the loads stay global loads)
         asm volatile("" : "+v"(rl));
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const f32x4_t v = rl[(s * kWidth + 16 * cb) / 4];
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
     if (HAS_P) {
         const float* prow = P + (size_t)tr * kD + c0 + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const float4 pv = *reinterpret_cast<const float4*>(prow + s * kWidth + 16 * cb);
@@ -703,11 +707,36 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
         if (R_commit && t < T) {
             float* crow = R_commit + (size_t)t * kD + c0 + 4 * g;
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     *reinterpret_cast<float4*>(crow + s * kWidth + 16 * cb) = rv[cb][s];
         }
+    }
+    if constexpr (CB == 1) {
+        // 16 columns: lane (n, g) holds token t, columns c0 + 4 g .. +3 of
+        // every stream; the 4 lanes of a token store 64 contiguous bytes
+        const float r[4][4] = {{rv[0][0].x, rv[0][0].y, rv[0][0].z, rv[0][0].w},
+                               {rv[0][1].x, rv[0][1].y, rv[0][1].z, rv[0][1].w},
+                               {rv[0][2].x, rv[0][2].y, rv[0][2].z, rv[0][2].w},
+                               {rv[0][3].x, rv[0][3].y, rv[0][3].z, rv[0][3].w}};
+        float m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m[i] = (acc[0][0][i] * r[0][i] + acc[0][1][i] * r[1][i]) + (acc[0][2][i] * r[2][i] + acc[0][3][i] * r[3][i]);
+        if (t < T) {
+            const size_t o = (size_t)t * kWidth + c0 + 4 * g;
+            *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
+            uint32_t bh[4], hh[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
+                hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
+            }
+            *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
+            *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+        return;
     }
     // The wave's 16 tokens x 64 columns of mixed go through 4 KB of LDS of its
     // own (inside ring slot 1, which the last step does not read) so that
@@ -842,10 +871,13 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        const int grid3 = 8 * kGroupsPerXcd * tiles;
         float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
-        auto* up = Pc ? (bf16_lo ? prefill_upmix<true, true> : prefill_upmix<true, false>)
-                      : (bf16_lo ? prefill_upmix<false, true> : prefill_upmix<false, false>);
+        const bool narrow = tiles <= 4;  // 16-column tiles (measured: better up to 256 tokens)
+        const int grid3 = (narrow ? 4 : 1) * 8 * kGroupsPerXcd * tiles;
+        auto* up = narrow ? (Pc ? (bf16_lo ? prefill_upmix<true, true, 1> : prefill_upmix<true, false, 1>)
+                                : (bf16_lo ? prefill_upmix<false, true, 1> : prefill_upmix<false, false, 1>))
+                          : (Pc ? (bf16_lo ? prefill_upmix<true, true, 4> : prefill_upmix<true, false, 4>)
+                                : (bf16_lo ? prefill_upmix<false, true, 4> : prefill_upmix<false, false, 4>));
         hipLaunchKernelGGL(up, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc, out_mixed + out_off,
                            out_bf16 + out_off, out_fp16 + out_off, Cc);
         e = hipGetLastError();

@@ -259,19 +259,21 @@ def test_full_size_configs_sampled(config):
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="config%d sampled" % config)
 
 
-@pytest.mark.parametrize("T, pending", [(128, False), (129, True), (384, False), (385, True), (1024, True),
-                                        (1025, False), (3968, False), (3969, True), (4097, False), (4097, True)])
+@pytest.mark.parametrize("T, pending", [(128, False), (129, True), (256, True), (257, False), (384, False),
+                                        (385, True), (1024, True), (1025, False), (3968, False), (3969, True),
+                                        (4097, False), (4097, True)])
 def test_wide_path_boundaries(T, pending):
     """Token counts at the wide path's internal boundaries: one token past a
-    128-token down tile; the down projection's K-split count changes from 80
-    (128-column splits) to 32 after 384 tokens, to 16 (stream quarters) after
-    1024 and to 8 (stream halves) after 3968; one token past a 4096-token
-    chunk (the second chunk holds a single token).  Oracle on the tokens
-    around each boundary plus a random sample."""
+    128-token down tile; the up+mix tile changes from 16 to 64 columns after
+    256 tokens (4 token tiles); the down projection's K-split count changes
+    from 80 (128-column splits) to 32 after 384 tokens, to 16 (stream
+    quarters) after 1024 and to 8 (stream halves) after 3968; one token past a
+    4096-token chunk (the second chunk holds a single token).  Oracle on the
+    tokens around each boundary plus a random sample."""
     _case("wide path boundary: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(5 if pending else 3, T=T, seed=T)
     gpu = hip_read(to_device(inp))
-    edges = {t for b in (64, 127, 128, 129, 384, 1024, 3968, 4095, 4096) for t in (b - 1, b) if 0 <= t < T}
+    edges = {t for b in (64, 127, 128, 129, 256, 384, 1024, 3968, 4095, 4096) for t in (b - 1, b) if 0 <= t < T}
     toks = np.array(sorted(set(_sample_tokens(T, k=24, seed=T).tolist()) | edges))
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="T=%d pending=%s" % (T, pending))
 
