@@ -37,6 +37,20 @@ std::map<int, bool> g_device_ok;
 // not run yet).  Guarded by g_check_mutex, which is taken before g_mutex.
 std::mutex g_check_mutex;
 std::map<int, bool> g_short_window;
+// Short-window launches of one device are ordered across streams.  Each needs
+// all 256 of its workgroups resident at once (one per CU); two running at the
+// same time could each get only part of the chip, and both would then wait
+// until their bounded waits expire.  Per device: the stream of the last
+// short-window launch, and an event.  A launch on another stream records the
+// event on that stream (covering its last launch) and waits for it; reads on
+// one stream record nothing (an event per read measured +3.5 us for a read
+// followed by other work).  Guarded by g_mutex.
+struct ShortOrder {
+    hipEvent_t done = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
+};
+std::map<int, ShortOrder> g_short_order;
 
 int record(hipError_t e, int status)
 {
@@ -292,22 +306,42 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
     if (st != HC_OK)
         return st;
 
-    if (T <= hc::kDecSplitMaxT && short_ok) {
-        // A short window: one launch per range of at most kDecMaxT consecutive tokens
-        // (ranges of near-equal size).  Every token's read is independent of
-        // the others, so the split changes no result.
-        const int n = static_cast<int>((T + hc::kDecMaxT - 1) / hc::kDecMaxT);
-        int t0 = 0;
-        for (int c = 0; c < n; ++c) {
-            const int left = static_cast<int>(T) - t0, chunks = n - c;
-            const int tc = (left + chunks - 1) / chunks;
-            const size_t in = static_cast<size_t>(t0) * hc::kD, out = static_cast<size_t>(t0) * hc::kWidth;
-            hipError_t e = hc::launch_decode(tc, R + in, pending ? pending + in : nullptr, w_norm, W_down, W_up,
-                                             out_mixed + out, out_bf16 + out, out_fp16 + out,
-                                             R_commit ? R_commit + in : nullptr, ws->dec, hs);
-            if (e != hipSuccess)
-                return record(e, HC_ERR_LAUNCH);
-            t0 += tc;
+    if (T <= hc::kDecMaxT && short_ok) {
+        // A short window: one launch of the short-window kernel, after the
+        // last short-window launch on any other stream of this device (not
+        // under graph capture: the caller orders the replays of a graph).
+        std::lock_guard<std::mutex> lock(g_mutex);
+        ShortOrder& so = g_short_order[dev];
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(hs, &cap);
+        if (e != hipSuccess)
+            return record(e, HC_ERR_LAUNCH);
+        const bool order = cap == hipStreamCaptureStatusNone;
+        if (order && so.used && so.last != hs) {
+            // after everything enqueued so far on the stream of the last
+            // short-window launch; if that stream is gone (HIP rejects the
+            // handle) or capturing, after everything on the device
+            bool ordered = false;
+            hipStreamCaptureStatus lc = hipStreamCaptureStatusActive;
+            if (hipStreamIsCapturing(so.last, &lc) == hipSuccess && lc == hipStreamCaptureStatusNone) {
+                if (!so.done && hipEventCreateWithFlags(&so.done, hipEventDisableTiming) != hipSuccess)
+                    so.done = nullptr;
+                ordered = so.done && hipEventRecord(so.done, so.last) == hipSuccess &&
+                          hipStreamWaitEvent(hs, so.done, 0) == hipSuccess;
+            }
+            if (!ordered) {
+                (void)hipGetLastError();
+                (void)hipDeviceSynchronize();
+                (void)hipGetLastError();
+            }
+        }
+        e = hc::launch_decode(static_cast<int>(T), R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16,
+                              R_commit, ws->dec, hs);
+        if (e != hipSuccess)
+            return record(e, HC_ERR_LAUNCH);
+        if (order) {
+            so.last = hs;
+            so.used = true;
         }
         return HC_OK;
     }
@@ -441,6 +475,13 @@ HC_API void hc_release(void)
         delete ws;
     }
     g_workspaces.clear();
+    for (auto& kv : g_short_order) {
+        if (kv.second.done) {
+            (void)hipSetDevice(kv.first);
+            (void)hipEventDestroy(kv.second.done);
+        }
+    }
+    g_short_order.clear();
     (void)hipSetDevice(cur);
 }
 

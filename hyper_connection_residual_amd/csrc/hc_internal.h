@@ -31,10 +31,6 @@ constexpr float kEps = 1e-6f;
 // polled by the consumer.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 32;
-// Up to this many tokens a read runs as ceil(T / kDecMaxT) short-window
-// launches over consecutive token ranges (one launch while T <= kDecMaxT);
-// beyond it the wide path costs less than streaming the weights once per range.
-constexpr int kDecSplitMaxT = 32;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;

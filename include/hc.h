@@ -33,7 +33,14 @@
  * stream), allocated on the first call on that stream (and grown once for a
  * larger T on the wide path); later calls allocate nothing.  Calls on
  * different streams never share scratch.  Calls on ONE stream are ordered by
- * the stream and are safe.
+ * the stream and are safe.  Short-window reads (T <= 32) use every CU of the
+ * device and must not run at the same time: the library orders them across
+ * streams.  A short-window read on another stream than the device's last one
+ * first waits for everything enqueued so far on that last stream (an event
+ * recorded there; if that stream was destroyed or is capturing, the call
+ * synchronizes the device instead).  Reads on one stream pay nothing for
+ * this.  Under graph capture the library does not order: the caller orders
+ * the replays of a graph.
  *
  * Errors: argument checks (T < 1, a null required pointer, misalignment, a
  * device that is not gfx950) happen before anything is enqueued and leave the

@@ -401,6 +401,35 @@ def test_two_streams_have_separate_scratch():
         assert np.array_equal(ga, ref_a) and np.array_equal(gb, ref_b)
 
 
+def test_short_window_reads_on_three_streams():
+    """Short-window reads issued back to back on three streams with no host
+    synchronisation in between (each launch needs every CU; the library
+    orders them across streams): every result equals the same read run alone,
+    and no bounded wait expired."""
+    import torch
+    from hyper_connection_residual_amd import binding
+    _case("short-window reads on three streams, T=8, 5 and 24, 12 rounds, no host sync")
+    cases = [wl.config_inputs(2, T=T, weight_set=ws) for T, ws in ((8, 40), (5, 41), (24, 42))]
+    devs = [to_device(c) for c in cases]
+    refs = [hip_read(d) for d in devs]
+    streams = [torch.cuda.Stream() for _ in devs]
+    outs = [(torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.float32, device="cuda"),
+             torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.int16, device="cuda"),
+             torch.empty((d["R"].shape[0], d["R"].shape[2]), dtype=torch.int16, device="cuda")) for d in devs]
+    torch.cuda.synchronize()
+    for st in streams:
+        binding.hc_timeouts(st)  # (reset the counters)
+    for _ in range(12):
+        for d, o, st in zip(devs, outs, streams):
+            assert binding.hc_read(d["R"].shape[0], d["R"], d["pending"], d["w_norm"], d["W_down"], d["W_up"],
+                                   o[0], o[1], o[2], st) == 0
+    torch.cuda.synchronize()
+    assert [binding.hc_timeouts(st) for st in streams] == [0, 0, 0]
+    for o, ref in zip(outs, refs):
+        assert np.array_equal(o[0].cpu().numpy().view(np.uint32), ref[0].view(np.uint32))
+        assert np.array_equal(o[1].cpu().numpy().view(np.uint16), ref[1].view(np.uint16))
+
+
 def test_graph_replay_matches_eager():
     """Reads captured in a HIP graph (short windows with pending, and one wide
     read) replay to the same bits as eager reads, replay after replay, with
