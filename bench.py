@@ -11,7 +11,7 @@ on the next weight set).  Inputs are resident in HBM before timing starts.
 Prints ONE JSON line.  `value` = weight bytes streamed per second over the
 timed sweeps (GB/s), one hc_read call per read; the same sweeps replayed from
 captured HIP graphs (one graph per step) are reported under `graph`.  Per-T
-microseconds per read, the times of windows of 9..64 tokens, the read with
+microseconds per read, the times of reads of 9..512 tokens, the read with
 the pending write committed (hc_read_commit) against the read plus a separate
 R += pending, and the prefill read times are reported beside it.  The
 roofline object describes the short-window kernel; the CPU baseline is the
@@ -35,7 +35,7 @@ TOKEN_BYTES_P = 4 * 2560 * 4 * 2 + 2560 * (4 + 2 + 2)  # R and pending read, mix
 HBM_PEAK_GBPS = 8000.0
 N_SETS = 48
 TS = list(range(1, 9))
-WINDOWS = [9, 12, 16, 17, 24, 32, 33, 48, 64]  # windows above 8 tokens, timed beside the sweep
+WINDOWS = [9, 12, 16, 17, 24, 32, 33, 48, 64, 128, 256, 512]  # reads above 8 tokens, timed beside the sweep
 
 
 def parse():
@@ -176,8 +176,8 @@ def main():
     print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
     del step_graphs
 
-    # ---- windows of 9..64 tokens (up to 16: one short-window launch, up to
-    # 32: two; beyond: the wide path), eager, weights rotated over the 48 sets
+    # ---- reads of 9..512 tokens (up to 32: one short-window launch; beyond:
+    # the wide path), eager, weights rotated over the 48 sets
     from hyper_connection_residual_amd import workloads as wl
     us_windows = {}
     for T in WINDOWS:
