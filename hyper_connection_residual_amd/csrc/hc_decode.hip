@@ -682,7 +682,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         } else {
             // token pairs: lane group k takes pairs k + 4 q (q < NQ: tokens
             // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows
-            constexpr int NQ = kTokSlots<T> / 8;
+            constexpr int NQ = (T + 7) / 8;  // pair groups holding tokens (the slots past them are padding)
             int pidx[kDecRedRows];
 #pragma unroll
             for (int rr = 0; rr < kDecRedRows; ++rr) {
