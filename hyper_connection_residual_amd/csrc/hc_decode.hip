@@ -41,7 +41,7 @@
 //   when 3 T <= 16, and 2, 3 or 6 chains for more tokens.
 // * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): 14
 //   of its 32 workgroups each reduce the 32 partials of 3 rows through the
-//   XCD's L2 (hop 1) and publish lo device-wide; every workgroup gathers all of lo
+//   XCD's L2 (hop 1, one wave; two above 16 tokens) and publish lo device-wide; every workgroup gathers all of lo
 //   (hop 2).  Hand-off words are 64 bits holding the payload and the launch's
 //   generation number, written once with one store; a consumer polls the data
 //   words themselves (device-coherent loads, which see a write-through store
@@ -601,7 +601,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (!reducer)
         issue_up();
 
-    if (wave == 0 && reducer) {
+    // above 16 tokens two waves share hop 1 (pair groups 0-1 and 2-3)
+    constexpr int kHopWaves = T > 16 ? 2 : 1;
+    if (wave < kHopWaves && reducer) {
         // (9) hop 1: lo rows 3 u .. 3 u + 2 of this group from its 32
         //     workgroups' partials, each stream's rs from its 8 slices' sums
         //     of squares; lo published device-wide.  Lane src + 16 k holds
@@ -681,8 +683,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     st_word(&s.lo[lo_word<T>(y, x, u, src, k)], word);
         } else {
             // token pairs: lane group k takes pairs k + 4 q (q < NQ: tokens
-            // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows
-            constexpr int NQ = (T + 7) / 8;  // pair groups holding tokens (the slots past them are padding)
+            // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows.  Only the pair groups
+            // holding tokens are reduced (the slots past them are padding);
+            // with two hop waves wave w takes groups 2 w + q, q < 2, and a
+            // group past the tokens re-reads the last one (no conditional
+            // polling load) and publishes nothing.
+            constexpr int NQT = (T + 7) / 8;               // pair groups holding tokens
+            constexpr int NQ = kHopWaves == 2 ? 2 : NQT;   // pair groups of this wave
+            const int qb = kHopWaves == 2 ? 2 * wave : 0;  // its first group
+            int qo[NQ];                                    // word offsets of its groups
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                qo[q] = 8 * (qb + q < NQT ? qb + q : NQT - 1);
             int pidx[kDecRedRows];
 #pragma unroll
             for (int rr = 0; rr < kDecRedRows; ++rr) {
@@ -698,11 +710,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 for (int q = 0; q < NQ; ++q) {
 #pragma unroll
                     for (int rr = 0; rr < kDecRedRows; ++rr) {
-                        wa_[rr][q] = ld_words2(s.part, pa0 * kTokSlots<T> + pidx[rr] + 8 * q);
-                        wb_[rr][q] = ld_words2(s.part, pb0 * kTokSlots<T> + pidx[rr] + 8 * q);
+                        wa_[rr][q] = ld_words2(s.part, pa0 * kTokSlots<T> + pidx[rr] + qo[q]);
+                        wb_[rr][q] = ld_words2(s.part, pb0 * kTokSlots<T> + pidx[rr] + qo[q]);
                     }
-                    qa_[q] = ld_words2(s.ssq, sa0 + 2 * k + 8 * q);
-                    qb_[q] = ld_words2(s.ssq, sb0 + 2 * k + 8 * q);
+                    qa_[q] = ld_words2(s.ssq, sa0 + 2 * k + qo[q]);
+                    qb_[q] = ld_words2(s.ssq, sb0 + 2 * k + qo[q]);
                 }
                 bool ok = true;
 #pragma unroll
@@ -737,12 +749,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                                                __uint_as_float(h ? qa_[q].z : qa_[q].x),
                                                __uint_as_float(h ? qb_[q].z : qb_[q].x));
             // lane src of group k writes row (src / 2) % 4 (row 3: padding),
-            // token 2 k + src % 2 + 8 q for q = src / 8 (+ 2 w: with 4 pair
-            // groups each lane writes two words)
+            // token 2 k + src % 2 + 8 (qb + q) for q = src / 8 (+ 2 w: with
+            // 3 or 4 pair groups in one wave each lane writes two words)
             constexpr int NW = NQ > 2 ? 2 : 1;
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) {
-                const int rr = (src >> 1) & 3, h = src & 1, q = (src >> 3) + 2 * w2, tok = 2 * k + h + 8 * q;
+                const int rr = (src >> 1) & 3, h = src & 1, q = (src >> 3) + 2 * w2, tok = 2 * k + h + 8 * (qb + q);
                 float mine = 0.f;
 #pragma unroll
                 for (int qq = 0; qq < NQ; ++qq)
@@ -753,7 +765,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
 #pragma unroll
                 for (int y = 0; y < kDecXcds; ++y)
-                    if (q < NQ)
+                    if (q < NQ && qb + q < NQT)
                         st_word(&s.lo[lo_word<T>(y, x, u, tok, rr)], word);
             }
         }
