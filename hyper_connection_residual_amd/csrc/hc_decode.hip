@@ -41,7 +41,7 @@
 //   when 3 T <= 16, and 2, 3 or 6 chains for more tokens.
 // * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): 14
 //   of its 32 workgroups each reduce the 32 partials of 3 rows through the
-//   XCD's L2 (hop 1, one wave; two above 16 tokens) and publish lo device-wide; every workgroup gathers all of lo
+//   XCD's L2 (hop 1, one wave; two above 8 tokens) and publish lo device-wide; every workgroup gathers all of lo
 //   (hop 2).  Hand-off words are 64 bits holding the payload and the launch's
 //   generation number, written once with one store; a consumer polls the data
 //   words themselves (device-coherent loads, which see a write-through store
@@ -601,8 +601,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (!reducer)
         issue_up();
 
-    // above 16 tokens two waves share hop 1 (pair groups 0-1 and 2-3)
-    constexpr int kHopWaves = T > 16 ? 2 : 1;
+    // above 8 tokens two waves share hop 1 (each takes half the pair groups)
+    constexpr int kHopWaves = T > 8 ? 2 : 1;
     if (wave < kHopWaves && reducer) {
         // (9) hop 1: lo rows 3 u .. 3 u + 2 of this group from its 32
         //     workgroups' partials, each stream's rs from its 8 slices' sums
@@ -685,12 +685,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             // token pairs: lane group k takes pairs k + 4 q (q < NQ: tokens
             // 2 k + 8 q, 2 k + 8 q + 1), all 3 rows.  Only the pair groups
             // holding tokens are reduced (the slots past them are padding);
-            // with two hop waves wave w takes groups 2 w + q, q < 2, and a
+            // with two hop waves wave w takes groups NQ w + q, q < NQ, and a
             // group past the tokens re-reads the last one (no conditional
             // polling load) and publishes nothing.
-            constexpr int NQT = (T + 7) / 8;               // pair groups holding tokens
-            constexpr int NQ = kHopWaves == 2 ? 2 : NQT;   // pair groups of this wave
-            const int qb = kHopWaves == 2 ? 2 * wave : 0;  // its first group
+            constexpr int NQT = (T + 7) / 8;                         // pair groups holding tokens
+            constexpr int NQ = kHopWaves == 2 ? (NQT + 1) / 2 : NQT;  // pair groups of this wave
+            const int qb = NQ * wave;                                // its first group
             int qo[NQ];                                    // word offsets of its groups
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
