@@ -38,11 +38,21 @@
  *        -- #1370 "What it does" (mixed with its BF16 / FP16 images).
  *
  * Weights are bf16 bit patterns, widened exactly from the format's fields.
- * fp64 mode is the parity reference: every quantity after R' is a double.
- * fp32 mode is a diagnostic: the same loops with float accumulators and the
- * two roundings of xn (product stored, then scaled), as the Norm bullet of
- * #315 describes.  Build with -O2 -ffp-contract=off and without fast-math so
- * the arithmetic is exactly what is written.
+ * Three modes:
+ *   fp64 (mode 0) is the parity reference: every quantity after R' is a
+ *        double.
+ *   fp32 (mode 1) is a diagnostic: the same loops with float accumulators,
+ *        each sum taken in ascending index order one rounded addition at a
+ *        time, rs = 1 / sqrtf(fl(ss / C) + eps), and the two roundings of xn
+ *        (R' * w_norm stored, then scaled by rs), as the Norm bullet of #315
+ *        describes.
+ *   bf16-lo (mode 2) is the fp64 read with lo rounded to bf16 (nearest, ties
+ *        to even) before the up projection: the operand the fused up + mix
+ *        of #1370 "What it does" feeds its BF16 mma (FP32 accumulation).  It
+ *        is the reference of the library's bf16-lo mode; lo itself (lo_out)
+ *        is reported before the rounding.
+ * Build with -O2 -ffp-contract=off and without fast-math so the arithmetic is
+ * exactly what is written.
  */
 #include <math.h>
 #include <stddef.h>
@@ -175,7 +185,7 @@ typedef struct {
     double* lo_out;
     const double* wd; /* widened weights (shared, read only) */
     const double* wu;
-    int mode; /* 0 = fp64, 1 = fp32 */
+    int mode; /* 0 = fp64, 1 = fp32, 2 = fp64 with lo rounded to bf16 */
     int64_t t_begin, t_end;
     int status;
 } oracle_job;
@@ -221,6 +231,10 @@ static void read_token_f64(const oracle_job* jb, int64_t t, double* rp,
     }
     if (jb->lo_out)
         memcpy(jb->lo_out + t * r, lo, sizeof(double) * (size_t)r);
+    /* bf16-lo mode: the up projection's operand is lo rounded to bf16 */
+    if (jb->mode == 2)
+        for (int j = 0; j < r; ++j)
+            lo[j] = isfinite(lo[j]) ? round_to_format(lo[j], 8, -126, 127) : lo[j];
     /* up projection; epilogue = identity */
     for (int64_t k = 0; k < D; ++k) {
         const double* wrow = jb->wu + k * r;
@@ -302,7 +316,7 @@ static void* run_job(void* arg)
 {
     oracle_job* jb = (oracle_job*)arg;
     const int64_t D = (int64_t)jb->n * jb->C;
-    size_t elt = jb->mode == 0 ? sizeof(double) : sizeof(float);
+    size_t elt = jb->mode == 1 ? sizeof(float) : sizeof(double);
     void* rp = malloc(elt * (size_t)D);
     void* xn = malloc(elt * (size_t)D);
     void* lo = malloc(elt * (size_t)jb->r);
@@ -311,10 +325,10 @@ static void* run_job(void* arg)
         jb->status = HC_ORACLE_ENOMEM;
     } else {
         for (int64_t t = jb->t_begin; t < jb->t_end; ++t) {
-            if (jb->mode == 0)
-                read_token_f64(jb, t, rp, xn, lo, up);
-            else
+            if (jb->mode == 1)
                 read_token_f32(jb, t, rp, xn, lo, up);
+            else
+                read_token_f64(jb, t, rp, xn, lo, up);
         }
         jb->status = HC_ORACLE_OK;
     }
@@ -330,7 +344,8 @@ static void* run_job(void* arg)
  *   R, P       fp32 [T][n][C]; P may be NULL (no pending write)
  *   w_norm     fp32 [n][C]
  *   W_down     bf16 bits [r][n*C];  W_up bf16 bits [n*C][r]
- *   mode       0 = fp64 (parity reference), 1 = fp32 (diagnostic)
+ *   mode       0 = fp64 (parity reference), 1 = fp32 (diagnostic),
+ *              2 = fp64 with lo rounded to bf16 before the up projection
  *   threads    >= 1; tokens are split into contiguous ranges, one per thread
  *              (every token is computed by the same code, so the result does
  *              not depend on the thread count)
@@ -344,7 +359,7 @@ int hc_oracle_read(int64_t T, int n, int C, int r, double eps,
                    double* mixed, double* rs_out, double* lo_out)
 {
     if (T < 0 || n < 1 || C < 1 || r < 1 || !(eps >= 0.0) || !R || !w_norm ||
-        !W_down || !W_up || !mixed || (mode != 0 && mode != 1) || threads < 1)
+        !W_down || !W_up || !mixed || mode < 0 || mode > 2 || threads < 1)
         return HC_ORACLE_EARG;
     if (T == 0)
         return HC_ORACLE_OK;

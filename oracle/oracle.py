@@ -77,6 +77,9 @@ def oracle_read(R, w_norm, W_down, W_up, pending=None, *, eps=1e-6,
 
     R, pending: float32 [T, n, C]; w_norm float32 [n, C];
     W_down: uint16 (bf16 bits) [r, n*C]; W_up: uint16 [n*C, r].
+    mode: "f64" (the parity reference), "f32" (diagnostic) or "f64_bf16_lo"
+    (the fp64 read with lo rounded to bf16 before the up projection: the
+    reference of the library's bf16-lo mode; lo is returned unrounded).
     Returns mixed as float64 [T, C] (plus rs [T, n] and lo [T, r] on request).
     """
     lib = load()
@@ -97,7 +100,7 @@ def oracle_read(R, w_norm, W_down, W_up, pending=None, *, eps=1e-6,
     mixed = np.empty((T, C), dtype=np.float64)
     rs = np.empty((T, n), dtype=np.float64) if want_rs else None
     lo = np.empty((T, r), dtype=np.float64) if want_lo else None
-    m = {"f64": 0, "f32": 1}[mode]
+    m = {"f64": 0, "f32": 1, "f64_bf16_lo": 2}[mode]
     st = lib.hc_oracle_read(T, n, C, r, float(eps), _ptr(R), _ptr(pending),
                             _ptr(w_norm), _ptr(W_down), _ptr(W_up), m,
                             int(threads), _ptr(mixed), _ptr(rs), _ptr(lo))

@@ -347,6 +347,151 @@ def test_threads_do_not_change_bits():
     assert np.array_equal(a, b)
 
 
+# --------------------------------------------------------------------------
+# The fp32 mode (diagnostic): pinned by hand-derived cases in which the
+# rounding of each step is forced, so that each of its stated rules (two
+# roundings of xn, every sum one rounded addition at a time in ascending
+# order, eps inside the square root next to the mean) changes the result
+# if it is broken.  u = 2^-23 is the binary32 spacing just above 1.
+# --------------------------------------------------------------------------
+
+def _one_hot_bf16(shape, entries):
+    W = np.zeros(shape, np.float32)
+    for idx, v in entries.items():
+        W[idx] = v
+    return _bf16(W)
+
+
+def _f32_read(R, w, Wd, Wu, eps, mode="f32"):
+    return orc.oracle_read(np.asarray(R, np.float32), np.asarray(w, np.float32), Wd, Wu,
+                           eps=eps, mode=mode)
+
+
+def test_fp32_mode_toy_case_exact():
+    """Every intermediate of the toy case is exact in binary32 too (rs of the
+    streams the down projection reads are 1/2 and 1/4; stream 2's rs = fl(1/3)
+    times 3 rounds back to 1), so the fp32 mode gives the exact output."""
+    n, C, r = 4, 8, 2
+    sig = np.array([1 if c % 2 == 0 else -1 for c in range(C)], np.float32)
+    R = np.stack([(s + 1) * sig for s in range(n)])[None].astype(np.float32)
+    Wd = np.zeros((r, n * C), np.float32)
+    Wd[0, 8:16] = sig
+    Wd[1, 24] = 0.5
+    Wu = np.zeros((n * C, r), np.float32)
+    Wu[0:8, 0] = 0.125
+    Wu[16:24, 1] = np.arange(C)
+    m = _f32_read(R, np.ones((n, C)), _bf16(Wd), _bf16(Wu), 0.0)
+    assert m[0].tolist() == [1.0, -2.5, 4.0, -5.5, 7.0, -8.5, 10.0, -11.5]
+
+
+def test_fp32_mode_rounds_xn_twice():
+    """n = C = r = 1, R' = 3, w_norm = 1 + u, W = 1, eps = 0.  rs = fl(1/3) =
+    11184811 * 2^-25.  First rounding: 3 (1 + u) = 3 + 1.5 * 2^-22 is a tie
+    between 3 + 2^-22 (odd) and 3 + 2^-21 (even): 3 + 2^-21.  Second: (3 +
+    2^-21) rs = 1 + 2^-25 + 11184811 * 2^-46 = 1 + 1.58 u -> 1 + 2u.  The mix
+    then gives 3 (1 + 2u) = 3 + 3 * 2^-22, exact (binary32 values in [2, 4)
+    are 2^-22 apart).  One rounding of R' w rs = 1 + 1.25 u would give 1 + u
+    and the output fl(3 + 1.5 * 2^-22) = 3 + 2^-21 (tie to even); the exact
+    read is 3 (1 + u)."""
+    one = _bf16(np.ones((1, 1)))
+    R = np.full((1, 1, 1), 3.0)
+    w = np.full((1, 1), 1 + 2.0 ** -23)
+    assert _f32_read(R, w, one, one, 0.0)[0, 0] == 3 + 3 * 2.0 ** -22
+    assert _f32_read(R, w, one, one, 0.0, mode="f64")[0, 0] == 3 * (1 + 2.0 ** -23)
+
+
+def test_fp32_mode_sums_in_ascending_order():
+    """Each sum adds one term at a time, index ascending, rounding each
+    addition: 1 + 2^-24 + 2^-24 + 2^-24 is then 1 (every step is a tie that
+    goes to the even 1), where the exact sum is 1 + 3 * 2^-24, a descending
+    order gives 1 + 2^-22, a pairwise order 1 + 2^-23 and a binary64
+    accumulator rounded at the end 1 + 2^-22.  One case per sum."""
+    e = 2.0 ** -24
+    # (a) the down projection's dot: n = 1, C = 4, r = 1, xn = 1
+    Wd = _one_hot_bf16((1, 4), {(0, 0): 1.0, (0, 1): e, (0, 2): e, (0, 3): e})
+    Wu = _bf16(np.ones((4, 1)))
+    m = _f32_read(np.ones((1, 1, 4)), np.ones((1, 4)), Wd, Wu, 0.0)
+    assert m[0].tolist() == [1.0, 1.0, 1.0, 1.0]
+    # (b) the up projection's dot: n = C = 1, r = 4, lo = (1, e, e, e)
+    Wd = _one_hot_bf16((4, 1), {(0, 0): 1.0, (1, 0): e, (2, 0): e, (3, 0): e})
+    Wu = _bf16(np.ones((1, 4)))
+    assert _f32_read(np.ones((1, 1, 1)), np.ones((1, 1)), Wd, Wu, 0.0)[0, 0] == 1.0
+    # (c) the mix over the streams: n = 4, C = r = 1, up = (1, e, e, e), R' = 1
+    Wd = _one_hot_bf16((1, 4), {(0, 0): 1.0})
+    Wu = _one_hot_bf16((4, 1), {(0, 0): 1.0, (1, 0): e, (2, 0): e, (3, 0): e})
+    assert _f32_read(np.ones((1, 4, 1)), np.ones((4, 1)), Wd, Wu, 0.0)[0, 0] == 1.0
+    # (d) the sum of squares: n = 1, C = 4, R' = (1, 2^-12, 2^-12, 2^-12): the
+    #     squares sum to 1, mean 1/4, rs = 2 exactly, and the read selects
+    #     xn[0] = 2 and mixes it with R'[0] = 1.  Summed exactly (1 + 3 e) the
+    #     mean is 1/4 + 0.75 e and rs is below 2.
+    R = np.array([[[1.0, 2.0 ** -12, 2.0 ** -12, 2.0 ** -12]]])
+    Wd = _one_hot_bf16((1, 4), {(0, 0): 1.0})
+    Wu = _one_hot_bf16((4, 1), {(0, 0): 1.0})
+    m = _f32_read(R, np.ones((1, 4)), Wd, Wu, 0.0)
+    assert m[0].tolist() == [2.0, 0.0, 0.0, 0.0]
+    assert _f32_read(R, np.ones((1, 4)), Wd, Wu, 0.0, mode="f64")[0, 0] < 2.0
+
+
+def test_fp32_mode_eps_goes_under_the_root_with_the_mean():
+    """n = 1, C = 2, R' = (1, 1), eps = 3: mean 1, rs = 1/sqrt(1 + 3) = 1/2.
+    (eps added to the sum of squares before the mean: 1/sqrt(2.5); added
+    after the root: 1/4.)  xn = 1/2, lo = xn[0], up = (lo, lo), mixed = up."""
+    Wd = _one_hot_bf16((1, 2), {(0, 0): 1.0})
+    Wu = _bf16(np.ones((2, 1)))
+    m = _f32_read(np.ones((1, 1, 2)), np.ones((1, 2)), Wd, Wu, 3.0)
+    assert m[0].tolist() == [0.5, 0.5]
+
+
+# --------------------------------------------------------------------------
+# The bf16-lo mode: the fp64 read with lo rounded to bf16 (nearest, ties to
+# even) before the up projection.  The toy case with lo[1] = 0.5 + d, where
+# bf16 values next to 0.5 are 2^-8 apart: mixed[c] = sigma_c (1 + 3 c lo[1]).
+# --------------------------------------------------------------------------
+
+def _toy_lo1(extra, mode):
+    n, C, r = 4, 8, 2
+    sig = np.array([1 if c % 2 == 0 else -1 for c in range(C)], np.float32)
+    R = np.stack([(s + 1) * sig for s in range(n)])[None].astype(np.float32)
+    Wd = np.zeros((r, n * C), np.float32)
+    Wd[0, 8:16] = sig
+    Wd[1, 24] = 0.5
+    for c, v in extra.items():  # stream 3, even columns: xn = +1
+        Wd[1, 24 + c] = v
+    Wu = np.zeros((n * C, r), np.float32)
+    Wu[0:8, 0] = 0.125
+    Wu[16:24, 1] = np.arange(C)
+    return orc.oracle_read(R, np.ones((n, C), np.float32), _bf16(Wd), _bf16(Wu), None,
+                           eps=0.0, mode=mode, want_lo=True)
+
+
+def _toy_mixed(lo1):
+    return [(1 if c % 2 == 0 else -1) * (1 + 3 * c * lo1) for c in range(8)]
+
+
+def test_bf16_lo_mode_toy_case_exact():
+    """lo = (8, 0.5) is exact in bf16: the mode gives the exact read."""
+    m, lo = _toy_lo1({}, "f64_bf16_lo")
+    assert lo[0].tolist() == [8.0, 0.5]
+    assert m[0].tolist() == [1.0, -2.5, 4.0, -5.5, 7.0, -8.5, 10.0, -11.5]
+
+
+def test_bf16_lo_mode_rounds_to_nearest_even():
+    """lo[1] = 0.5 + 2^-9 is a tie between 0.5 (even) and 0.5 + 2^-8: it
+    rounds to 0.5.  lo[1] = 0.5 + 2^-9 + 2^-10 lies above the tie: 0.5 +
+    2^-8.  lo[1] = 0.5 + 2^-10 lies below it: 0.5.  (Truncation would give
+    0.5 for all three, rounding ties up 0.5 + 2^-8 for the first.)  lo is
+    reported unrounded, and the fp64 mode keeps the exact value."""
+    for extra, rounded in (({2: 2.0 ** -9}, 0.5),
+                           ({2: 2.0 ** -9, 4: 2.0 ** -10}, 0.5 + 2.0 ** -8),
+                           ({4: 2.0 ** -10}, 0.5)):
+        exact = 0.5 + sum(extra.values())
+        m, lo = _toy_lo1(extra, "f64_bf16_lo")
+        assert lo[0, 1] == exact
+        assert m[0].tolist() == _toy_mixed(rounded)
+        m64, _ = _toy_lo1(extra, "f64")
+        np.testing.assert_allclose(m64[0], _toy_mixed(exact), rtol=1e-15)
+
+
 def test_fp32_mode_is_at_fp32_level():
     # Two fp32 implementations agree to about 1e-7 relative on the pages (the
     # fused read against the pair); a plain sequential fp32 dot over 10240
