@@ -14,8 +14,12 @@ captured HIP graphs (one graph per step) are reported under `graph`.  Per-T
 microseconds per read, the times of reads of 9..512 tokens, the read with
 the pending write committed (hc_read_commit) against the read plus a separate
 R += pending, and the prefill read times are reported beside it.  The
-roofline object describes the short-window kernel; the CPU baseline is the
-plain oracle on the host.
+roofline object describes the short-window kernel, next to `stream_floor_us`:
+one launch of that kernel's shape that only streams 13,148,160 bytes (48
+rotated buffers, cold), the floor for a single launch moving the weights.  The
+CPU baseline is the plain oracle on the host, on all its cores (one read per
+core) and on one.  The run prints a hash of the kernel sources it was built
+from, so a profiler run's summary can be tied to the kernels it measured.
 """
 from __future__ import annotations
 
@@ -50,6 +54,8 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (the reference for "
                          "scaling the HBM byte counters of a profiler run)")
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="host cores for the all-core oracle leg (0: all, at most 16)")
     ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_wide_reads_hbm_bytes.md"),
                     help="summary of the profiler's FETCH_SIZE / WRITE_SIZE runs; its figure is "
                          "reported only if it was measured on the current kernel source")
@@ -76,6 +82,53 @@ def make_sets(torch):
     return sets, acts
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args):
+    """The oracle (fp64, as it stands) on the host over a bounded sample of the
+    sweep: reads cycling T = 1..8 and the weight sets.  All-core leg: one read
+    per core at a time (each read single-threaded; the oracle releases the
+    interpreter while it runs); then a one-core leg.  Weight bytes per second."""
+    import concurrent.futures as cf
+    from oracle import oracle as orc
+    from hyper_connection_residual_amd import workloads as wl
+    nproc = os.cpu_count() or 1
+    cores = args.cpu_cores or min(16, nproc)
+    inputs = [wl.config_inputs(2, T=TS[i % len(TS)], weight_set=i % N_SETS) for i in range(2 * cores)]
+
+    def one(inp):
+        orc.oracle_read(inp.R, inp.w_norm, inp.W_down, inp.W_up, inp.pending, threads=1)
+
+    legs = {}
+    for n in (cores, 1):
+        budget = args.cpu_seconds / 2
+        reads, t0 = 0, time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=n) as pool:
+            while time.perf_counter() - t0 < budget:
+                list(pool.map(one, [inputs[(reads + j) % len(inputs)] for j in range(n)]))
+                reads += n
+        wall = time.perf_counter() - t0
+        legs[n] = (reads, wall)
+    reads, wall = legs[cores]
+    r1, w1 = legs[1]
+    return {"value": round(reads * WEIGHT_BYTES / wall / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d oracle reads (fp64, one read per core at a time, %d cores of %d, %s) of the T=1..8 "
+                      "verify-window sweep with pending, cycling T and weight sets, %.1f s wall"
+                      % (reads, cores, nproc, _cpu_model(), wall),
+            "one_core": {"value": round(r1 * WEIGHT_BYTES / w1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "sample": "%d reads, %.1f s" % (r1, w1)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -87,6 +140,9 @@ def main():
     from hyper_connection_residual_amd import binding
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     binding.library()
+    from hyper_connection_residual_amd import rocprof_summary
+    src_hash = rocprof_summary.source_hash()
+    print("# kernel source hash: %s" % src_hash, file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -140,41 +196,24 @@ def main():
         us_eager[str(T)] = round(ms * 1e3 / 300, 3)
     print("# eager us per read by T: %s" % us_eager, file=sys.stderr, flush=True)
 
-    # ---- HIP graphs: each step position of the rotation captured once (8
-    # reads per graph) and replayed; the same reads, inputs and outputs as the
-    # eager run.  Scratch of the capture stream is created eagerly first.
-    gstream = torch.cuda.Stream()
-    with torch.cuda.stream(gstream):
-        for T in TS:
-            read_on(T, 0, gstream)
-    torch.cuda.synchronize()
-    step_graphs = []
-    for j in range(n_pos):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=gstream):
-            for i, T in enumerate(TS):
-                read_on(T, (len(TS) * j + i) % N_SETS, gstream)
-        step_graphs.append(g)
-    for k in range(args.warmup):
-        with torch.cuda.stream(gstream):
-            step_graphs[k % n_pos].replay()
-    t0 = time.perf_counter()
-    ms_graph = time_region(gstream, lambda k: step_graphs[k % n_pos].replay(), args.steps)
-    print("# graph: %d steps, %.3f ms/step (event), wall %.3f s"
-          % (args.steps, ms_graph / args.steps, time.perf_counter() - t0), file=sys.stderr, flush=True)
-    us_graph = {}
-    for T in TS:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=gstream):
-            for m in range(N_SETS):
-                read_on(T, m, gstream)
-        with torch.cuda.stream(gstream):
-            g.replay()
-        ms = time_region(gstream, lambda k, g=g: g.replay(), 6)
-        us_graph[str(T)] = round(ms * 1e3 / (6 * N_SETS), 3)
-        del g
-    print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
-    del step_graphs
+    # ---- the floor: one launch of the short-window kernel's shape that only
+    # streams WEIGHT_BYTES from memory (48 rotated buffers, 631 MB, cold)
+    floor_bufs = [torch.empty(WEIGHT_BYTES // 4, dtype=torch.float32, device=dev).fill_(float(m))
+                  for m in range(N_SETS)]
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+
+    def stream_once(k):
+        st = binding.hc_stream_read(floor_bufs[k % N_SETS], WEIGHT_BYTES, sink, stream.cuda_stream)
+        if st != 0:
+            raise binding.HCError(st, "hc_stream_read")
+
+    for k in range(N_SETS):
+        stream_once(k)
+    ms_floor = time_region(stream, stream_once, 300)
+    floor_us = round(ms_floor * 1e3 / 300, 3)
+    print("# stream floor: %.3f us per launch (%.0f GB/s)" % (floor_us, WEIGHT_BYTES / (floor_us * 1e-6) / 1e9),
+          file=sys.stderr, flush=True)
+    del floor_bufs
 
     # ---- reads of 9..512 tokens (up to 32: one short-window launch; beyond:
     # the wide path), eager, weights rotated over the 48 sets
@@ -243,9 +282,7 @@ def main():
     # average launch duration (back-to-back launches on one stream)
     alg_bytes_per_step = sum(WEIGHT_BYTES + T * TOKEN_BYTES_P for T in TS)
     achieved = alg_bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    timeouts = binding.hc_timeouts(stream) + binding.hc_timeouts(gstream)
-    if timeouts:
-        print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
+    timeouts = binding.hc_timeouts(stream)
 
     if args.calib_copy:
         src = torch.empty(256 << 18, dtype=torch.float32, device=dev).fill_(1.0)
@@ -256,9 +293,8 @@ def main():
         del src, dst
 
     traffic = None
-    from hyper_connection_residual_amd import rocprof_summary
     measured = rocprof_summary.read_traffic(args.traffic_md)
-    if measured and measured[1] == rocprof_summary.source_hash():
+    if measured and measured[1] == src_hash:
         traffic = measured[0]  # HBM bytes per launch, sweep average
 
     prefill = None
@@ -319,26 +355,50 @@ def main():
         del R5, P5, Wd, Wu
         prefill = prefill_all["T8192"]
 
+    # ---- HIP graphs (last: the first calls on the capture stream make the
+    # library order short-window reads across streams for a while, which the
+    # eager legs above must not pay): each step position of the rotation captured once (8
+    # reads per graph) and replayed; the same reads, inputs and outputs as the
+    # eager run.  Scratch of the capture stream is created eagerly first.
+    gstream = torch.cuda.Stream()
+    with torch.cuda.stream(gstream):
+        for T in TS:
+            read_on(T, 0, gstream)
+    torch.cuda.synchronize()
+    step_graphs = []
+    for j in range(n_pos):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for i, T in enumerate(TS):
+                read_on(T, (len(TS) * j + i) % N_SETS, gstream)
+        step_graphs.append(g)
+    for k in range(args.warmup):
+        with torch.cuda.stream(gstream):
+            step_graphs[k % n_pos].replay()
+    t0 = time.perf_counter()
+    ms_graph = time_region(gstream, lambda k: step_graphs[k % n_pos].replay(), args.steps)
+    print("# graph: %d steps, %.3f ms/step (event), wall %.3f s"
+          % (args.steps, ms_graph / args.steps, time.perf_counter() - t0), file=sys.stderr, flush=True)
+    us_graph = {}
+    for T in TS:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for m in range(N_SETS):
+                read_on(T, m, gstream)
+        with torch.cuda.stream(gstream):
+            g.replay()
+        ms = time_region(gstream, lambda k, g=g: g.replay(), 6)
+        us_graph[str(T)] = round(ms * 1e3 / (6 * N_SETS), 3)
+        del g
+    print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
+    del step_graphs
+    timeouts += binding.hc_timeouts(stream) + binding.hc_timeouts(gstream)
+    if timeouts:
+        print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
+
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-        from hyper_connection_residual_amd import workloads as wl
-        reads, weight_bytes, spent = 0, 0, 0.0
-        T_cycle = TS
-        i = 0
-        while spent < args.cpu_seconds:
-            T = T_cycle[i % len(T_cycle)]
-            inp = wl.config_inputs(2, T=T, weight_set=i % N_SETS)
-            t = time.perf_counter()
-            orc.oracle_read(inp.R, inp.w_norm, inp.W_down, inp.W_up, inp.pending, threads=1)
-            spent += time.perf_counter() - t
-            reads += 1
-            weight_bytes += WEIGHT_BYTES
-            i += 1
-        cpu = {"value": round(weight_bytes / spent / 1e9, 4), "unit": "GB/s",
-               "cores": 1, "kind": "oracle",
-               "sample": "%d oracle reads (fp64, one thread) of the T=1..8 verify-window sweep "
-                         "with pending, cycling T and weight sets, %.1f s of CPU time" % (reads, spent)}
+        cpu = cpu_baseline(args)
         print("# cpu baseline: %s" % cpu, file=sys.stderr, flush=True)
 
     line = {
@@ -369,7 +429,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "stream_floor_us": floor_us,
         "timeouts": timeouts,
+        "kernel_source_hash": src_hash,
     }
     print(json.dumps(line), flush=True)
 

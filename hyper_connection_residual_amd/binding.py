@@ -34,6 +34,8 @@ SIGNATURES = {
     "hc_dims": (None, [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)]),
     "hc_timeouts": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32)]),
+    "hc_stream_read": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
+    "hc_release_stream": (ctypes.c_int, [_P]),
     "hc_release": (None, []),
 }
 
@@ -108,7 +110,7 @@ def hc_read_bf16_lo(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, ou
 
 
 def hc_short_window_on() -> bool:
-    """Whether the current device reads windows of up to 24 tokens with the
+    """Whether the current device reads windows of up to 32 tokens with the
     short-window kernel (the library's start-up check decides; it runs now if
     it has not yet)."""
     on = ctypes.c_int()
@@ -140,21 +142,44 @@ def hc_timeouts(stream=None) -> int:
     return cnt.value
 
 
+def hc_stream_read(src, nbytes, sink, stream=None):
+    """hc_stream_read of the C ABI (a measurement reference): one launch that
+    streams `nbytes` of the device buffer `src` and writes sink[256].
+    Returns the status code."""
+    return library().hc_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
+
+
+def hc_release_stream(stream=None) -> None:
+    st = library().hc_release_stream(_stream(stream))
+    if st != HC_OK:
+        raise HCError(st, "hc_release_stream")
+
+
 def hc_release() -> None:
     library().hc_release()
 
 
-def _check(t, name, dtype, shape):
+def _check_kind(t, name, dtype, shape):
+    """dtype and shape (checked for every argument before any device check)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
-    if t.dtype != dtype:
+    if isinstance(dtype, tuple):
+        if t.dtype not in dtype:
+            raise TypeError("%s must be one of %s, got %s" % (name, dtype, t.dtype))
+    elif t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if tuple(t.shape) != tuple(shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_place(t, name):
     if not t.is_cuda:
         raise ValueError("%s must be on the GPU" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+_BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
 def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None, commit=False):
@@ -163,31 +188,36 @@ def read(R, w_norm, W_down, W_up, pending=None, out=None, stream=None, commit=Fa
     R, pending: float32 [T, 4, 2560]; w_norm: float32 [4, 2560];
     commit=True also writes R + pending back into R (hc_read_commit);
     W_down: bf16 bits as int16/uint16 [320, 10240] (or a torch.bfloat16 tensor);
-    W_up: [10240, 320] likewise.  Returns (mixed float32 [T, 2560],
-    bf16 image as torch.bfloat16 [T, 2560], fp16 image as torch.float16 [T, 2560]).
+    W_up: [10240, 320] likewise.  out: optional (mixed float32 [T, 2560],
+    bf16 image as bfloat16 / int16 / uint16, fp16 image as float16 / int16 /
+    uint16).  Returns (mixed float32 [T, 2560], bf16 image as torch.bfloat16
+    [T, 2560], fp16 image as torch.float16 [T, 2560]) unless `out` is given.
     """
     n, C, r, _ = hc_dims()
-    T = int(R.shape[0]) if R.dim() == 3 else -1
-    _check(R, "R", torch.float32, (T, n, C))
-    if T == 0:  # nothing to read: empty outputs, no launch
-        return (torch.empty((0, C), dtype=torch.float32, device=R.device),
-                torch.empty((0, C), dtype=torch.bfloat16, device=R.device),
-                torch.empty((0, C), dtype=torch.float16, device=R.device))
+    if not isinstance(R, torch.Tensor) or R.dim() != 3:
+        raise ValueError("R must be a [T, %d, %d] tensor" % (n, C))
+    T = int(R.shape[0])
+    args = [(R, "R", torch.float32, (T, n, C)), (w_norm, "w_norm", torch.float32, (n, C)),
+            (W_down, "W_down", _BITS16, (r, n * C)), (W_up, "W_up", _BITS16, (n * C, r))]
     if pending is not None:
-        _check(pending, "pending", torch.float32, (T, n, C))
-    _check(w_norm, "w_norm", torch.float32, (n, C))
-    for name, W, shape in (("W_down", W_down, (r, n * C)), ("W_up", W_up, (n * C, r))):
-        if W.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-            raise TypeError("%s must hold bf16 bits (bfloat16, int16 or uint16)" % name)
-        _check(W, name, W.dtype, shape)
+        args.append((pending, "pending", torch.float32, (T, n, C)))
+    if out is not None:
+        mixed, img_bf16, img_fp16 = out
+        # the images are 16-bit patterns: bf16 bits (bfloat16, or int16 /
+        # uint16 holding them) and fp16 bits (float16, int16 or uint16)
+        args += [(mixed, "out_mixed", torch.float32, (T, C)), (img_bf16, "out_bf16", _BITS16, (T, C)),
+                 (img_fp16, "out_fp16", (torch.float16, torch.int16, torch.uint16), (T, C))]
+    for a in args:
+        _check_kind(*a)
+    for a in args:
+        _check_place(a[0], a[1])
     if out is None:
         out = (torch.empty((T, C), dtype=torch.float32, device=R.device),
                torch.empty((T, C), dtype=torch.bfloat16, device=R.device),
                torch.empty((T, C), dtype=torch.float16, device=R.device))
+    if T == 0:  # nothing to read: no launch
+        return out
     mixed, img_bf16, img_fp16 = out
-    _check(mixed, "out_mixed", torch.float32, (T, C))
-    _check(img_bf16, "out_bf16", img_bf16.dtype, (T, C))
-    _check(img_fp16, "out_fp16", img_fp16.dtype, (T, C))
     fn = hc_read_commit if commit else hc_read
     st = fn(T, R, pending, w_norm, W_down, W_up, mixed, img_bf16, img_fp16, stream)
     if st != HC_OK:

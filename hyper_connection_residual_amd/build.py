@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhc.so")
 
-SOURCES = ["hc_api.hip", "hc_decode.hip", "hc_prefill.hip"]
+SOURCES = ["hc_api.hip", "hc_decode.hip", "hc_prefill.hip", "hc_stream.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

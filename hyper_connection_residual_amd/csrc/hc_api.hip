@@ -23,7 +23,7 @@ thread_local int g_last_hip_error = 0;
 
 struct Workspace {
     int device = 0;
-    hipStream_t stream = nullptr;
+    hipStream_t stream = nullptr;  // (used only while the caller's stream is live: calls on it, hc_release_stream)
     void* dec_base = nullptr;
     hc::DecodeScratch dec{};
     void* wide_base = nullptr;
@@ -31,7 +31,11 @@ struct Workspace {
 };
 
 std::mutex g_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace*> g_workspaces;
+// Workspaces by (device, stream handle value).  A stream that HIP creates with
+// the handle of a destroyed one (its memory can be reused only once the old
+// stream's work has finished) takes over that workspace; hc_release_stream
+// frees a workspace before its stream is destroyed.
+std::map<std::pair<int, uintptr_t>, Workspace*> g_workspaces;
 std::map<int, bool> g_device_ok;
 // Result of the start-up check of the short-window kernel per device (absent:
 // not run yet).  Guarded by g_check_mutex, which is taken before g_mutex.
@@ -40,15 +44,24 @@ std::map<int, bool> g_short_window;
 // Short-window launches of one device are ordered across streams.  Each needs
 // all 256 of its workgroups resident at once (one per CU); two running at the
 // same time could each get only part of the chip, and both would then wait
-// until their bounded waits expire.  Per device: the stream of the last
-// short-window launch, and an event.  A launch on another stream records the
-// event on that stream (covering its last launch) and waits for it; reads on
-// one stream record nothing (an event per read measured +3.5 us for a read
-// followed by other work).  Guarded by g_mutex.
+// until their bounded waits expire.  Per device: which stream made the last
+// short-window launch (its handle value, only compared, never passed to HIP).
+// A launch on another stream than the last one waits for the last launch:
+// through an event recorded right after it, if there is one, else by
+// synchronizing the device.  Events are recorded only while streams
+// alternate: a switch turns recording on, and 64 launches in a row on one
+// stream turn it off again, since an event per read costs +3.5 us (measured
+// for a read followed by other work) and a stream's reads are ordered by the
+// stream itself.  No handle of another stream is ever used.  Guarded by
+// g_mutex.
+constexpr int kQuietLaunches = 64;
 struct ShortOrder {
     hipEvent_t done = nullptr;
-    hipStream_t last = nullptr;
-    bool used = false;
+    uintptr_t last = 0;     // stream handle value of the last launch
+    bool used = false;      // a launch has been ordered on this device
+    bool recording = false; // an event follows every launch
+    bool recorded = false;  // `done` covers the last launch
+    int quiet = 0;          // launches on the last stream since the last switch
 };
 std::map<int, ShortOrder> g_short_order;
 
@@ -61,6 +74,23 @@ int record(hipError_t e, int status)
 bool aligned16(const void* p)
 {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// The key of a stream: its handle value (never dereferenced).
+uintptr_t stream_key(hipStream_t stream)
+{
+    return reinterpret_cast<uintptr_t>(stream);
+}
+
+// The bounded waits' limit of ordinary reads: HC_WAIT_TICKS (ticks of the
+// 100 MHz clock) if set, else 50 ms.  Read once.
+long long read_wait_ticks()
+{
+    static const long long ticks = [] {
+        const char* v = std::getenv("HC_WAIT_TICKS");
+        return v ? std::atoll(v) : hc::kDecWaitTicks;
+    }();
+    return ticks;
 }
 
 // The current device must be a gfx950 part.
@@ -86,7 +116,7 @@ int current_device(int* dev)
 int workspace(int dev, hipStream_t stream, Workspace** out)
 {
     std::lock_guard<std::mutex> lock(g_mutex);
-    auto key = std::make_pair(dev, stream);
+    auto key = std::make_pair(dev, stream_key(stream));
     auto it = g_workspaces.find(key);
     if (it != g_workspaces.end()) {
         *out = it->second;
@@ -171,14 +201,17 @@ struct CheckRng {
 // kernels check themselves once per card and fall back to the plain kernel
 // on any disagreement: "#315 hc: the multi-token hyper-connection read split
 // finer", Exactness).  Its hand-offs need all 256 workgroups resident at once
-// and the dispatcher's placement of workgroups on XCDs; the check reads 8
-// tokens with pending once through it and once through the wide path (which
-// needs neither) and keeps it only if (a) every workgroup fits, (b) no
-// bounded wait expired and (c) the two outputs agree to 4e-6 of their largest
-// value (each is within 2e-6 of the exact read).  Otherwise windows of up to
-// 32 tokens take the wide path.  The bounded waits' limit can be lowered with
-// HC_SELFCHECK_WAIT_TICKS (ticks of the 100 MHz clock) to force the
-// fallback.  One line per device goes to stderr (HC_LOG=0 silences it).
+// and the dispatcher's placement of workgroups on XCDs; the check reads one
+// window per code path of the kernel (1, 5, 9, 17 and 32 tokens, with
+// pending: one, two, three and six MFMA chains; hop 1 on rows, on token pairs
+// and on two waves; shared LDS regions) once through it and once through the
+// wide path (which needs neither) and keeps it only if (a) every workgroup
+// fits, (b) no bounded wait expired and (c) each pair of outputs agrees to
+// 4e-6 of its largest value (each is within 2e-6 of the exact read).
+// Otherwise windows of up to 32 tokens take the wide path.  The bounded
+// waits' limit can be lowered with HC_SELFCHECK_WAIT_TICKS (ticks of the 100
+// MHz clock) to force the fallback.  One line per device goes to stderr
+// (HC_LOG=0 silences it).
 int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t why_len)
 {
     *on = false;
@@ -197,8 +230,9 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     int st = wide_workspace(ws);
     if (st != HC_OK)
         return st;
-    constexpr int T = 8;
-    const size_t nin = (size_t)T * hc::kD, nw = (size_t)hc::kRank * hc::kD, nout = (size_t)T * hc::kWidth;
+    constexpr int kChecks[] = {1, 5, 9, 17, 32};
+    constexpr int TM = hc::kDecMaxT;
+    const size_t nin = (size_t)TM * hc::kD, nw = (size_t)hc::kRank * hc::kD, nout = (size_t)TM * hc::kWidth;
     CheckRng rng;
     std::vector<float> R(nin), P(nin), w(hc::kD);
     std::vector<uint16_t> Wd(nw), Wu(nw);
@@ -231,29 +265,42 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     if (e == hipSuccess) e = hipMemcpyAsync(dWd, Wd.data(), 2 * nw, hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = hipMemcpyAsync(dWu, Wu.data(), 2 * nw, hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
-    if (e == hipSuccess)
-        e = hc::launch_decode(T, dR, dP, dw, dWd, dWu, m1, img, img + nout, nullptr, ws->dec, hs, ticks);
-    if (e == hipSuccess)
-        e = hc::launch_prefill(T, dR, dP, dw, dWd, dWu, m2, img + 2 * nout, img + 3 * nout, nullptr, false,
-                               ws->wide_base, hc::kPrefillChunk, hs);
+    double worst = 0.0;
+    bool finite = true;
+    int worst_T = 0;
+    for (int T : kChecks) {
+        const size_t no = (size_t)T * hc::kWidth;
+        if (e == hipSuccess)
+            e = hc::launch_decode(T, dR, dP, dw, dWd, dWu, m1, img, img + nout, nullptr, ws->dec, hs, ticks);
+        if (e == hipSuccess)
+            e = hc::launch_prefill(T, dR, dP, dw, dWd, dWu, m2, img + 2 * nout, img + 3 * nout, nullptr, false,
+                                   ws->wide_base, hc::kPrefillChunk, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(a.data(), m1, 4 * no, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(b.data(), m2, 4 * no, hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e != hipSuccess)
+            break;
+        double dmax = 0.0, vmax = 0.0;
+        for (size_t i = 0; i < no; ++i) {
+            finite = finite && std::isfinite(a[i]) && std::isfinite(b[i]);
+            dmax = std::fmax(dmax, std::fabs((double)a[i] - (double)b[i]));
+            vmax = std::fmax(vmax, std::fabs((double)b[i]));
+        }
+        const double rel = vmax > 0.0 ? dmax / vmax : dmax;
+        if (!(rel <= worst) || worst_T == 0) {
+            worst = rel;
+            worst_T = T;
+        }
+    }
     if (e == hipSuccess) e = hipMemcpyAsync(&expired, ws->dec.timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost, hs);
     if (e == hipSuccess) e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
-    if (e == hipSuccess) e = hipMemcpyAsync(a.data(), m1, 4 * nout, hipMemcpyDeviceToHost, hs);
-    if (e == hipSuccess) e = hipMemcpyAsync(b.data(), m2, 4 * nout, hipMemcpyDeviceToHost, hs);
     if (e == hipSuccess) e = hipStreamSynchronize(hs);
     const hipError_t ef = hipFree(buf);
     if (e != hipSuccess || ef != hipSuccess)
         return record(e != hipSuccess ? e : ef, HC_ERR_DEVICE);
-    double dmax = 0.0, vmax = 0.0;
-    bool finite = true;
-    for (size_t i = 0; i < nout; ++i) {
-        finite = finite && std::isfinite(a[i]) && std::isfinite(b[i]);
-        dmax = std::fmax(dmax, std::fabs((double)a[i] - (double)b[i]));
-        vmax = std::fmax(vmax, std::fabs((double)b[i]));
-    }
-    const double rel = vmax > 0.0 ? dmax / vmax : dmax;
-    *on = expired == 0 && finite && rel <= 4e-6;
-    std::snprintf(why, why_len, "%u expired waits, agrees with the wide path to %.1e", expired, rel);
+    *on = expired == 0 && finite && worst <= 4e-6;
+    std::snprintf(why, why_len, "%u expired waits, %s, agrees with the wide path to %.1e (worst at %d tokens)",
+                  expired, finite ? "all finite" : "NOT all finite", worst, worst_T);
     return HC_OK;
 }
 
@@ -276,6 +323,56 @@ int short_window_on(int dev, Workspace* ws, bool* on)
         std::fprintf(stderr, "hc: device %d: the short-window read is %s (start-up check: %s)%s\n", dev,
                      *on ? "on" : "OFF", why, *on ? "" : "; windows of up to 32 tokens take the wide path");
     return HC_OK;
+}
+
+// One launch of the short-window kernel on `hs`, after the last short-window
+// launch on any other stream of this device (not under graph capture: the
+// caller orders the replays of a graph).
+hipError_t launch_short_window(int dev, hipStream_t hs, int T, const float* R, const float* pending,
+                               const float* w_norm, const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                               uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, const hc::DecodeScratch& scr)
+{
+    const uintptr_t id = stream_key(hs);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    ShortOrder& so = g_short_order[dev];
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(hs, &cap);
+    if (e != hipSuccess)
+        return e;
+    const bool order = cap == hipStreamCaptureStatusNone;
+    if (order && so.used && id != so.last) {
+        // a switch: after the last launch on the other stream
+        e = so.recorded ? hipStreamWaitEvent(hs, so.done, 0) : hipDeviceSynchronize();
+        if (e != hipSuccess)
+            return e;
+        so.recording = true;
+        so.quiet = 0;
+    } else if (order && so.recording && ++so.quiet >= kQuietLaunches) {
+        so.recording = false;  // one stream again: its own order suffices
+    }
+    e = hc::launch_decode(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, R_commit, scr, hs,
+                          read_wait_ticks());
+    if (e != hipSuccess)
+        return e;
+    if (order) {
+        so.recorded = false;
+        if (so.recording) {
+            if (!so.done) {
+                e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming);
+                if (e != hipSuccess) {
+                    so.done = nullptr;
+                    return e;
+                }
+            }
+            e = hipEventRecord(so.done, hs);
+            if (e != hipSuccess)
+                return e;
+            so.recorded = true;
+        }
+        so.last = id;
+        so.used = true;
+    }
+    return hipSuccess;
 }
 
 // The read of hc_read, hc_read_commit and hc_read_bf16_lo; R_commit is NULL
@@ -307,43 +404,9 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
         return st;
 
     if (T <= hc::kDecMaxT && short_ok) {
-        // A short window: one launch of the short-window kernel, after the
-        // last short-window launch on any other stream of this device (not
-        // under graph capture: the caller orders the replays of a graph).
-        std::lock_guard<std::mutex> lock(g_mutex);
-        ShortOrder& so = g_short_order[dev];
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        hipError_t e = hipStreamIsCapturing(hs, &cap);
-        if (e != hipSuccess)
-            return record(e, HC_ERR_LAUNCH);
-        const bool order = cap == hipStreamCaptureStatusNone;
-        if (order && so.used && so.last != hs) {
-            // after everything enqueued so far on the stream of the last
-            // short-window launch; if that stream is gone (HIP rejects the
-            // handle) or capturing, after everything on the device
-            bool ordered = false;
-            hipStreamCaptureStatus lc = hipStreamCaptureStatusActive;
-            if (hipStreamIsCapturing(so.last, &lc) == hipSuccess && lc == hipStreamCaptureStatusNone) {
-                if (!so.done && hipEventCreateWithFlags(&so.done, hipEventDisableTiming) != hipSuccess)
-                    so.done = nullptr;
-                ordered = so.done && hipEventRecord(so.done, so.last) == hipSuccess &&
-                          hipStreamWaitEvent(hs, so.done, 0) == hipSuccess;
-            }
-            if (!ordered) {
-                (void)hipGetLastError();
-                (void)hipDeviceSynchronize();
-                (void)hipGetLastError();
-            }
-        }
-        e = hc::launch_decode(static_cast<int>(T), R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16,
-                              R_commit, ws->dec, hs);
-        if (e != hipSuccess)
-            return record(e, HC_ERR_LAUNCH);
-        if (order) {
-            so.last = hs;
-            so.used = true;
-        }
-        return HC_OK;
+        hipError_t e = launch_short_window(dev, hs, static_cast<int>(T), R, pending, w_norm, W_down, W_up,
+                                           out_mixed, out_bf16, out_fp16, R_commit, ws->dec);
+        return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
     }
     st = wide_workspace(ws);
     if (st != HC_OK)
@@ -442,7 +505,7 @@ HC_API int hc_timeouts(void* stream, uint32_t* count)
     Workspace* ws = nullptr;
     {
         std::lock_guard<std::mutex> lock(g_mutex);
-        auto it = g_workspaces.find(std::make_pair(dev, hs));
+        auto it = g_workspaces.find(std::make_pair(dev, stream_key(hs)));
         if (it == g_workspaces.end())
             return HC_OK;
         ws = it->second;
@@ -456,6 +519,44 @@ HC_API int hc_timeouts(void* stream, uint32_t* count)
     if (e != hipSuccess)
         return record(e, HC_ERR_DEVICE);
     *count = v;
+    return HC_OK;
+}
+
+HC_API int hc_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream)
+{
+    if (!src || !sink || bytes < 16 || bytes % 16 != 0)
+        return HC_ERR_ARG;
+    if (!aligned16(src) || !aligned16(sink))
+        return HC_ERR_ALIGN;
+    int dev = 0;
+    int st = current_device(&dev);
+    if (st != HC_OK)
+        return st;
+    const hipError_t e = hc::launch_stream(src, bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
+}
+
+HC_API int hc_release_stream(void* stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_DEVICE);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    auto it = g_workspaces.find(std::make_pair(dev, stream_key(hs)));
+    if (it == g_workspaces.end())
+        return HC_OK;
+    Workspace* ws = it->second;
+    e = hipStreamSynchronize(hs);
+    if (e != hipSuccess)
+        return record(e, HC_ERR_DEVICE);
+    if (ws->dec_base)
+        (void)hipFree(ws->dec_base);
+    if (ws->wide_base)
+        (void)hipFree(ws->wide_base);
+    delete ws;
+    g_workspaces.erase(it);
     return HC_OK;
 }
 

@@ -49,7 +49,10 @@
 //   load of a polling round in flight at once.  Every workgroup counts its
 //   launches in its own slot, so all of them agree on the generation without
 //   host involvement (the launch is graph-capture safe).  Every wait is
-//   bounded.
+//   bounded, and an expired wait never yields silent results: a reducer whose
+//   wait expired publishes NaN words marked as poison, and a workgroup whose
+//   own wait expired or that received poison stores NaN for every output it
+//   owns (and commits nothing).
 #include "hc_internal.h"
 
 // No multiply-add contraction anywhere in this file: a butterfly sum must give
@@ -277,6 +280,10 @@ __device__ __forceinline__ uint64_t tag_f32(float v, uint32_t gen)
 {
     return (uint64_t)__float_as_uint(v) | ((uint64_t)gen << 32);
 }
+// Generations count modulo 2^31; the top bit of a device-wide lo word's tag
+// marks poison: its producer's bounded wait expired and its payload is NaN.
+constexpr uint32_t kGenMask = 0x7fffffffu;
+constexpr uint32_t kPoison = 0x80000000u;
 // Tag of a word handed over inside one XCD: the generation and the
 // producer's dispatch rotation (see the kernel).
 __device__ __forceinline__ uint32_t xcd_tag(uint32_t gen, uint32_t rot)
@@ -353,6 +360,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     uint16_t* const lpl = reinterpret_cast<uint16_t*>(lds + kOffLo<T> / 16);              // [3 T][kLoRow]
     float* const rpl = reinterpret_cast<float*>(lds + kOffRp<T> / 16);                    // [T][40]
     f32x4_t* const ucomb = reinterpret_cast<f32x4_t*>(lds + kOffUComb<T> / 16);           // [3][chains][64]
+    // set by a wave whose hop-2 wait expired or that received poison: the
+    // workgroup then stores NaN outputs and commits nothing
+    __shared__ uint32_t poisoned_wg;
 
     DecodeScratch s;
     s.part = scratch;
@@ -385,6 +395,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // (counted) wait, never as a silent stale read.
     const uint32_t rot = (__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) - (uint32_t)x) & 7u;
     HC_PROBE(0, threadIdx.x == 0);
+    if (threadIdx.x == 0)
+        poisoned_wg = 0;  // (ordered before any setter by the barriers B1, Bc1, Bs)
     const float* const Pm = P ? P : R;  // (a missing pending re-reads R)
 
     // ---- Loads.  The W_down tile, the activations of its columns and the
@@ -502,7 +514,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     wg_barrier();      // B1: y staged, W_down tile complete
     HC_PROBE(1, threadIdx.x == 0);
     pin(seen);
-    const uint32_t gen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u;
+    const uint32_t gen = ((uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u) & kGenMask;
 
     // (7) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
     //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over K
@@ -634,6 +646,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             const int pa = (pa0 + rowc) * kTokSlots<T>, pb = (pb0 + rowc) * kTokSlots<T>;
             uint4 wa_[NP], wb_[NP], qa_[NP], qb_[NP];
             [[maybe_unused]] int rounds = 0;
+            bool expired = false;  // (wave-uniform: the clock is a scalar read)
             while (true) {
                 ++rounds;
                 new_round();
@@ -657,6 +670,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 if (wall_clock64() - t0 > wait_ticks) {
                     if (lane == 0)
                         note_timeout(s.timeouts);
+                    expired = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -676,7 +690,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             // 32 words (2 whole lines) per replica: tokens 0..7 x rows 0..3 of
             // this reducer, 0 in the padding; lane src < 8 of group k writes
             // row k, token src
-            const uint64_t word = tag_f32(valid && src < T ? mine : 0.f, gen);
+            const uint64_t word = expired ? tag_f32(__builtin_nanf(""), gen | kPoison)
+                                          : tag_f32(valid && src < T ? mine : 0.f, gen);
 #pragma unroll
             for (int y = 0; y < kDecXcds; ++y)
                 if (src < 8)
@@ -703,6 +718,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             uint4 wa_[kDecRedRows][NQ], wb_[kDecRedRows][NQ], qa_[NQ], qb_[NQ];
             [[maybe_unused]] int rounds = 0;
+            bool expired = false;  // (wave-uniform)
             while (true) {
                 ++rounds;
                 new_round();
@@ -732,6 +748,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 if (wall_clock64() - t0 > wait_ticks) {
                     if (lane == 0)
                         note_timeout(s.timeouts);
+                    expired = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -762,7 +779,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                     for (int r3 = 0; r3 < kDecRedRows; ++r3)
                         mine = (qq == q && r3 == rr) ? (h ? lo[r3][qq][1] : lo[r3][qq][0]) : mine;
                 const bool valid = rr < kDecRedRows && kDecRedRows * u + rr < kDecRowsPerXcd && tok < T;
-                const uint64_t word = tag_f32(valid ? mine : 0.f, gen);
+                const uint64_t word = expired ? tag_f32(__builtin_nanf(""), gen | kPoison)
+                                              : tag_f32(valid ? mine : 0.f, gen);
 #pragma unroll
                 for (int y = 0; y < kDecXcds; ++y)
                     if (q < NQ && qb + q < NQT)
@@ -793,6 +811,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             widx[k] = lo_word<T>(x, wave, us, tt, 2 * pair);
         }
         [[maybe_unused]] int rounds = 0;
+        bool bad = false;  // this wave's wait expired, or a word it got is poison
         while (true) {
             ++rounds;
             new_round();
@@ -802,7 +821,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             bool all = true;
 #pragma unroll
             for (int k = 0; k < NS; ++k)
-                all = all && lw[k].y == gen && lw[k].w == gen;
+                all = all && (lw[k].y & kGenMask) == gen && (lw[k].w & kGenMask) == gen;
             if (__all(all)) {
                 HC_COUNT(2, 1, rounds, wave == 0 && lane == 0);
                 break;
@@ -810,9 +829,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             if (wall_clock64() - t0 > wait_ticks) {
                 if (lane == 0)
                     note_timeout(s.timeouts);
+                bad = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
+        }
+        bool got_poison = false;
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            got_poison = got_poison || ((lw[k].y | lw[k].w) & kPoison) != 0;
+        bad = bad || __any(got_poison);
+        if (bad) {
+            // NaN lo: the up projection then gives NaN for every token
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                lw[k].x = __float_as_uint(__builtin_nanf(""));
+                lw[k].z = lw[k].x;
+            }
+            if (lane == 0)
+                poisoned_wg = 1;
         }
         HC_PROBE(14, wave == 0 && lane == 0);
 #pragma unroll
@@ -849,15 +884,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
     wg_barrier();  // B2: lo and R' staged, W_up tile complete
     HC_PROBE(8, threadIdx.x == 0);
+    const bool poisoned = poisoned_wg != 0;
     // (10') the pending write committed: R' of this workgroup's 40 (stream,
     //      column) pairs back into R.  No read of these elements is left
     //      anywhere: every workgroup read them for its down part before it
     //      stored the partials that hop 2 has just waited for, and no other
-    //      workgroup mixes these columns.
+    //      workgroup mixes these columns.  (After an expired wait that is not
+    //      known: nothing is committed.)
 #pragma unroll
     for (int pp = 0; pp < kUpPasses; ++pp) {
         const int it = threadIdx.x + kDecThreads * pp;
-        if (R_commit && P && it < kUpRows * T) {
+        if (R_commit && P && !poisoned && it < kUpRows * T) {
             const int at = it / kUpRows, row = it - at * kUpRows;
             R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime[pp];
         }
@@ -915,7 +952,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             auto at = [&](int j) { return cf[(64 * j + n + 16 * (i16 >> 2)) * 4 + (i16 & 3)]; };
             const float up = tt < T ? (kSplitUp ? at(0) + (at(1) + at(2)) : piece_sum<T>(cf, 0, tt, n)) : 0.f;
             const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
-            const float mixed = sum4(up * rp);  // (s0 + s1) + (s2 + s3)
+            const float mixed = poisoned ? __builtin_nanf("") : sum4(up * rp);  // (s0 + s1) + (s2 + s3)
             if (owner && tt < T) {
                 const size_t o = (size_t)tt * kWidth + c;
                 out_mixed[o] = mixed;

@@ -81,4 +81,11 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
                           uint16_t* out_bf16, uint16_t* out_fp16, float* R_commit, bool bf16_lo,
                           void* scratch, int chunk, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Measurement reference: one launch of the short-window kernel's shape that
+// streams `bytes` (a multiple of 16, at least 16) from src into LDS and writes
+// one word per workgroup to sink[256].
+// ---------------------------------------------------------------------------
+hipError_t launch_stream(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace hc

@@ -1,5 +1,5 @@
-// hc_prefill.hip -- the hyper-connection read for wide inputs (T > 8 tokens):
-// prefill chunks and long verify windows.
+// hc_prefill.hip -- the hyper-connection read for wide inputs (T > 32 tokens):
+// prefill chunks and verify windows beyond the short-window kernel.
 //
 // The read is the one of "#315 hc: the multi-token hyper-connection read split
 // finer" with the norm folded into the down projection ("#2488 sycl/A770",
@@ -8,41 +8,47 @@
 // fp32) never leaves registers.  Three launches per chunk of up to 4096 tokens:
 //
 //   P1 down:  part[sig][t][j] = sum_{k in split sig} W_down[j][k] * (R'[t][k] *
-//             w_norm[k]) and ssq[sig][t] = sum_{k in sig} R'[t][k]^2, where the
-//             8 splits are the halves of the 4 streams (1280 columns each).
-//   P2 lo:    rs[t][s] = 1/sqrt(sum of stream s's two ssq / 2560 + eps) and
-//             lo[t][j] = sum_s rs[t][s] * (stream s's two partials), stored as
-//             three bf16 planes (an exact split of the fp32 value) in the
-//             tiled layout P3 copies into LDS verbatim.
-//   P3 up+mix: a tile of 64 tokens x 64 output columns x 4 streams: the up
-//             projection (K = 320) on the matrix cores, then the mix of the 4
-//             streams with R' and the bf16 / fp16 images, all in registers.
+//             w_norm[k]) and ssq[sig][t] = sum_{k in sig} R'[t][k]^2 over S
+//             column splits that lie inside the streams: S = 8 (stream
+//             halves, 1280 columns) for 4096-token chunks, 16 (quarters) for
+//             chunks of 1025..3968 tokens, 32 (320 columns) for 385..1024 and
+//             80 (128 columns) up to 384 tokens (splits_for).
+//   P2 lo:    rs[t][s] = 1/sqrt(sum of stream s's split ssq / 2560 + eps) and
+//             lo[t][j] = sum_s rs[t][s] * (stream s's split partials), stored
+//             in fp32 in the tiled layout P3 copies into LDS verbatim (P3
+//             splits each value into its three bf16 pieces in registers).
+//   P3 up+mix: a tile of 64 tokens x 64 output columns x 4 streams (16
+//             columns for chunks of at most 256 tokens): the up projection
+//             (K = 320) on the matrix cores, then the mix of the 4 streams with
+//             R' and the bf16 / fp16 images, all in registers.
 //
 // gfx950 design:
 // * Both matrix kernels run bf16 v_mfma_f32_16x16x32_bf16 with every fp32
 //   activation split exactly into three bf16 pieces (hi + mid + lo3 == x), so
 //   each product is exact and the result stays fp32-faithful.
-// * Weight operands (and P3's lo planes) go from memory straight into LDS
-//   (global_load_lds_dwordx4, 16 bytes a lane) through a two-stage ring, one K
-//   step of 32 ahead of the matrix cores.  LDS is read with inline-asm
-//   ds_read_b128 and every wait is explicit: the compiler, seeing an LDS read
-//   that may alias a load still landing in LDS, would wait for ALL loads in
-//   flight (vmcnt(0)) and serialise the ring.
+// * Weight operands (and P3's lo tiles, and P1's raw activations) go from
+//   memory straight into LDS (global_load_lds_dwordx4, 16 bytes a lane)
+//   through rings: P1 loads its W_down panel one K step of 32 ahead and raw R
+//   (and pending) two or three steps ahead; P3 runs a three-stage ring two
+//   steps ahead.  LDS is read with inline-asm ds_read_b128 and every wait is
+//   explicit: the compiler, seeing an LDS read that may alias a load still
+//   landing in LDS, would wait for ALL loads in flight (vmcnt(0)) and
+//   serialise the ring.
 // * Inside LDS a K step of a weight tile is a "panel": one row per matrix
 //   row, four 16-byte chunks per row, chunk c of row r stored at slot
 //   4 r + (c ^ ((r >> 1) & 3)).  LDS serves a 16-byte read to 8 lanes per
 //   cycle; the 8 lanes that read one chunk column of 8 consecutive rows then
 //   hit distinct bank groups (measured: the swizzle by r >> 2 instead left
 //   ~45 % of LDS cycles in bank conflicts).
-// * Both kernels use 4 waves and 56-64 KB of LDS, so two workgroups share a
-//   CU: one's epilogue (memory bound) overlaps the other's matrix work.
-// * XCD-aware grids (workgroup b runs on XCD b % 8): P1's XCD x owns split x,
-//   so its 820 KB W_down slice stays in that XCD's L2; P3's XCD x owns 5 of
-//   the 40 column groups (W_up slices, 820 KB) and walks the token tiles, the 5
-//   workgroups of one tile being dispatched together so its lo planes are read
-//   once per XCD.
-// * The chunk keeps a chunk's R (+ pending) within the 256 MB Infinity Cache
-//   for its second read in P3.
+// * P1 takes a whole CU (12 waves, up to 157 KB of LDS: 8 matrix waves and 4
+//   producer waves that load and convert); P3 uses 4 waves and 72 KB, so two
+//   workgroups share a CU and one's epilogue (memory bound) overlaps the
+//   other's matrix work.
+// * XCD-aware grids (workgroup b runs on XCD b % 8): with 8 splits P1's XCD x
+//   owns split x, so its 820 KB W_down slice stays in that XCD's L2; P3's XCD
+//   x owns 5 of the 40 column groups (W_up slices, 820 KB) and walks the token
+//   tiles, the 5 workgroups of one tile being dispatched together so its lo
+//   tile is read once per XCD.
 #include "hc_internal.h"
 
 #include <type_traits>

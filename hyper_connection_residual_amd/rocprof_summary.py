@@ -3,7 +3,7 @@
     python -m hyper_connection_residual_amd.rocprof_summary stats <kernel_stats.csv> > out.md
     python -m hyper_connection_residual_amd.rocprof_summary trace <kernel_trace.csv> > out.md
     python -m hyper_connection_residual_amd.rocprof_summary bytes <fetch counter_collection.csv> \
-        <write counter_collection.csv> > out.md
+        <write counter_collection.csv> <fetch run log> <write run log> > out.md
 
 `stats` tabulates per-kernel durations; `trace` does the same per (kernel,
 workgroup count), which separates launches of one kernel at different sizes.  `bytes` tabulates HBM bytes per
@@ -12,8 +12,10 @@ Both counters are scaled by what they read for a plain device-to-device copy of
 known size run in the same process (the runtime's copy kernel, which bench.py
 --calib-copy launches: 5 copies of 256 MiB); the scale factors are printed.  The
 short-window kernel's sweep average (T = 1..8) is printed on a line bench.py
-reads, together with a hash of the kernel source it was measured on, so a later
-change to the kernel makes bench.py report the traffic as unknown.
+reads, together with the hash of the kernel sources the profiled runs were
+built from, taken from those runs' own output (bench.py prints it; both runs
+must agree), so a later change to the kernels makes bench.py report the
+traffic as unknown.
 """
 from __future__ import annotations
 
@@ -25,13 +27,28 @@ import re
 import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-DECODE_SOURCE = os.path.join(_PKG, "csrc", "hc_decode.hip")
+CSRC = os.path.join(_PKG, "csrc")
 COPY_BYTES = 5 * (256 << 20)  # bench.py --calib-copy
 
 
-def source_hash(path: str = DECODE_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash() -> str:
+    """Hash of the library's kernel and host sources and its build flags."""
+    from hyper_connection_residual_amd import build
+    h = hashlib.sha256(" ".join(build.FLAGS).encode())
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def hash_in_log(path: str):
+    """The kernel source hash a bench.py run printed, or None."""
+    with open(path, errors="replace") as f:
+        for line in f:
+            m = re.search(r"kernel source hash: (\w+)", line)
+            if m:
+                return m.group(1)
+    return None
 
 
 def short_name(name: str) -> str:
@@ -73,7 +90,11 @@ def _per_kernel(path):
     return acc
 
 
-def traffic(fetch_path: str, write_path: str) -> str:
+def traffic(fetch_path: str, write_path: str, fetch_log: str, write_log: str) -> str:
+    hashes = {hash_in_log(fetch_log), hash_in_log(write_log)}
+    if len(hashes) != 1 or None in hashes:
+        raise SystemExit("the two profiled runs printed different (or no) kernel source hashes: %s" % hashes)
+    run_hash = hashes.pop()
     fetch, write = _per_kernel(fetch_path), _per_kernel(write_path)
     copy = "__amd_rocclr_copyBuffer"
     f_scale = COPY_BYTES / sum(fetch[copy]) if fetch.get(copy) else float("nan")
@@ -93,7 +114,7 @@ def traffic(fetch_path: str, write_path: str) -> str:
             sweep.append(rd + wt)
     if sweep:
         out += ["", "short-window kernel HBM bytes per launch (sweep average): %d" % round(sum(sweep) / len(sweep)),
-                "short-window kernel source hash: %s" % source_hash()]
+                "short-window kernel source hash: %s" % run_hash]
     return "\n".join(out)
 
 
@@ -119,6 +140,6 @@ if __name__ == "__main__":
     elif sys.argv[1] == "trace":
         print(trace(sys.argv[2]))
     elif sys.argv[1] == "bytes":
-        print(traffic(sys.argv[2], sys.argv[3]))
+        print(traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
     else:
         raise SystemExit(__doc__)

@@ -23,33 +23,49 @@
  *
  * Memory: every pointer argument is a DEVICE pointer (hipMalloc memory or any
  * device-accessible allocation), row-major, contiguous, 16-byte aligned.  The
- * caller owns all of them; the library only reads R, pending, w_norm, W_down
- * and W_up, and only writes the three outputs.  Outputs must not overlap any
- * input or each other.  R is not updated with R'.
+ * caller owns all of them; hc_read and hc_read_bf16_lo only read R,
+ * pending, w_norm, W_down and W_up and only write the three outputs
+ * (hc_read_commit also writes R).  Outputs must not overlap any input or
+ * each other.
  *
  * Execution: asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream).  No host synchronization; results are visible to later work on the
- * same stream.  The library keeps a small scratch workspace per (device,
- * stream), allocated on the first call on that stream (and grown once for a
- * larger T on the wide path); later calls allocate nothing.  Calls on
- * different streams never share scratch.  Calls on ONE stream are ordered by
- * the stream and are safe.  Short-window reads (T <= 32) use every CU of the
- * device and must not run at the same time: the library orders them across
- * streams.  A short-window read on another stream than the device's last one
- * first waits for everything enqueued so far on that last stream (an event
- * recorded there; if that stream was destroyed or is capturing, the call
- * synchronizes the device instead).  Reads on one stream pay nothing for
- * this.  Under graph capture the library does not order: the caller orders
- * the replays of a graph.
+ * same stream.  The library keeps a scratch workspace per (device, stream):
+ * 3.7 MB for the short-window kernel, allocated on the first call on that
+ * stream, and a fixed 87 MB for the wide path, allocated on the stream's
+ * first wide read; later calls allocate nothing.  Workspaces are found by
+ * the stream's handle value: call hc_release_stream before destroying a
+ * stream that ran reads (otherwise its workspace lives until hc_release, and
+ * a later stream that HIP gives the same handle takes it over, which is safe
+ * once the old stream's work has finished).  Calls on different streams never
+ * share scratch.  Calls on ONE stream are ordered by the stream and are safe.
+ * Short-window reads (T <= 32) use every CU of the device and must not run at
+ * the same time: the library orders them across streams.  A short-window
+ * read on another stream than the device's last one waits for that last
+ * read: through an event recorded right after it if there is one, else by
+ * synchronizing the device.  Events are recorded only while streams
+ * alternate: a switch of stream turns recording on (+3.5 us per read), and 64
+ * reads in a row on one stream turn it off again.  The library never calls
+ * HIP on a stream other than the one a call passes.  Under graph capture the
+ * library does not order: the caller orders the replays of a graph.
  *
  * Errors: argument checks (T < 1, a null required pointer, misalignment, a
  * device that is not gfx950) happen before anything is enqueued and leave the
- * outputs untouched.  A failed kernel launch returns HC_ERR_LAUNCH
- * (hc_last_hip_error() gives the hipError_t).  Device faults surface at the
- * caller's next synchronization, as in HIP.  The single-launch short-window
- * kernel waits on data from other workgroups with a bounded wait; if that wait
- * ever expires (its workgroups could not all be resident at once), the call
- * still completes, its outputs are invalid, and hc_timeouts() reports it.
+ * outputs untouched.  A failed kernel launch returns
+ * HC_ERR_LAUNCH (hc_last_hip_error() gives the hipError_t).  Device faults
+ * surface at the caller's next synchronization, as in HIP.  The single-launch
+ * short-window kernel waits on data from other workgroups with a bounded wait
+ * (50 ms).  If such a wait ever expires (the workgroups could not all be
+ * resident at once, e.g. another process or a long kernel on another stream
+ * held CUs), the read cannot produce its result; the call has already
+ * returned, so the kernel marks it in the outputs instead: every output value
+ * the affected workgroups own (all of them, once a reducer's wait expired) is
+ * stored as NaN, in out_mixed and in both images, hc_read_commit leaves those
+ * workgroups' part of R uncommitted, and hc_timeouts() counts the expired
+ * waits.  Outputs are therefore either the read's result or NaN, never silently
+ * wrong.  HC_WAIT_TICKS (ticks of the 100 MHz clock) lowers that limit for
+ * ordinary reads (0: every wait gives up at its first miss), which tests use
+ * to force the case.
  */
 #ifndef HC_H
 #define HC_H
@@ -152,9 +168,11 @@ HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, cons
  * 32 tokens with the short-window kernel, 0 if they take the wide path.  The
  * kernel's hand-offs need its 256 workgroups resident together and placed on
  * the XCDs the way it expects; once per device (on the first call of any
- * entry point that reads) the library reads 8 tokens through it and through
- * the wide path and keeps it only if every workgroup fits, no bounded wait
- * expired and the two outputs agree to 4e-6 of their largest value.  The
+ * entry point that reads) the library reads windows of 1, 5, 9, 17 and 32
+ * tokens (one per code path of the kernel) through it and through the wide
+ * path and keeps it only if every workgroup fits, no bounded wait expired,
+ * every output is finite and each pair of outputs agrees to 4e-6 of its
+ * largest value.  The
  * pages' reads check themselves the same way, once per card, bit for bit
  * against the plain variant ("#315 hc: the multi-token hyper-connection read
  * split finer", Exactness).  One line per device goes to stderr unless
@@ -177,14 +195,45 @@ HC_API void hc_dims(int* n, int* C, int* r, float* eps);
 
 /*
  * hc_timeouts -- number of expired bounded waits recorded in the workspace of
- * (current device, stream) since the last call, then resets it to zero.
+ * (current device, stream) since the last call, then resets it to zero (the
+ * reads concerned stored NaN outputs; see Errors above).
  * Synchronizes `stream`.  *count receives 0 when the stream has no workspace.
  * Returns HC_OK or an HC_ERR_* code.
  */
 HC_API int hc_timeouts(void* stream, uint32_t* count);
 
+/*
+ * hc_stream_read -- a measurement reference, not part of the read: one launch
+ * of the short-window kernel's shape (256 workgroups of 512 threads, one per
+ * CU) that streams `bytes` of `src` from memory into LDS with the whole-line
+ * loads its weight tiles use and computes nothing.  Its duration is the
+ * floor for a single launch moving that many bytes, against which the read's
+ * duration (13,148,160 weight bytes, "#2070 sm_75: a hyper-connection up
+ * kernel", the 13 MB of BF16 weights per read) is compared.
+ *
+ *   src     const device buffer of `bytes` bytes, 16-byte aligned
+ *   bytes   a multiple of 16, >= 16
+ *   sink    uint32_t[256] device buffer, 16-byte aligned: one word per
+ *           workgroup (keeps the loads live; its contents mean nothing)
+ *   stream  hipStream_t to run on (NULL = default stream)
+ *
+ * Asynchronous; allocates nothing.  Returns HC_OK, HC_ERR_ARG (null pointer,
+ * bytes < 16 or not a multiple of 16), HC_ERR_ALIGN, HC_ERR_DEVICE or
+ * HC_ERR_LAUNCH.
+ */
+HC_API int hc_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * hc_release_stream -- free the workspace of (current device, stream), after
+ * synchronizing that stream.  Call it before destroying a stream that ran
+ * reads, or the workspace stays allocated until hc_release.  Later calls on
+ * the stream allocate again.  Returns HC_OK (also when the stream has no
+ * workspace) or an HC_ERR_* code.
+ */
+HC_API int hc_release_stream(void* stream);
+
 /* Free every workspace the library holds on every device (synchronizes each
- * stream that has one).  Later calls allocate again. */
+ * device that has one).  Later calls allocate again. */
 HC_API void hc_release(void);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == ["hc_read", "hc_read_commit", "hc_read_bf16_lo", "hc_short_window_on", "hc_status_string",
-                     "hc_last_hip_error", "hc_dims", "hc_timeouts", "hc_release"]
+                     "hc_last_hip_error", "hc_dims", "hc_timeouts", "hc_stream_read", "hc_release_stream", "hc_release"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -84,6 +84,17 @@ def test_argument_checks_happen_before_any_hip_call(lib, entry):
         assert fn(1, *a, 0) == binding.HC_ERR_ALIGN, i
 
 
+def test_stream_read_checks_arguments_first(lib):
+    from hyper_connection_residual_amd import binding
+    good = 0x10000
+    assert binding.hc_stream_read(None, 1024, good, 0) == binding.HC_ERR_ARG
+    assert binding.hc_stream_read(good, 1024, None, 0) == binding.HC_ERR_ARG
+    assert binding.hc_stream_read(good, 8, good, 0) == binding.HC_ERR_ARG
+    assert binding.hc_stream_read(good, 1000, good, 0) == binding.HC_ERR_ARG
+    assert binding.hc_stream_read(good + 4, 1024, good, 0) == binding.HC_ERR_ALIGN
+    assert binding.hc_stream_read(good, 1024, good + 4, 0) == binding.HC_ERR_ALIGN
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
                     reason="a GPU is present; this checks the no-device error path")
 def test_no_device_is_an_error_not_a_fallback(lib):
@@ -108,3 +119,26 @@ def test_python_read_refuses_cpu_tensors(lib):
         binding.read(R, w, Wd, Wu)
     with pytest.raises(TypeError):
         binding.read(R.double(), w, Wd, Wu)
+
+
+def test_python_read_refuses_image_buffers_of_the_wrong_width(lib):
+    """The image outputs hold 16-bit patterns: a caller-supplied buffer of
+    1-byte (or 4-byte) elements is refused before any launch, since the
+    kernels store 2 bytes per element."""
+    import torch
+    from hyper_connection_residual_amd import binding
+    T = 2
+    R = torch.zeros((T, 4, 2560))
+    w = torch.ones((4, 2560))
+    Wd = torch.zeros((320, 10240), dtype=torch.int16)
+    Wu = torch.zeros((10240, 320), dtype=torch.int16)
+    mixed = torch.empty((T, 2560))
+    good = torch.empty((T, 2560), dtype=torch.int16)
+    for bad in (torch.uint8, torch.int8, torch.float32, torch.int32):
+        img = torch.empty((T, 2560), dtype=bad)
+        with pytest.raises(TypeError, match="out_bf16"):
+            binding.read(R, w, Wd, Wu, out=(mixed, img, good))
+        with pytest.raises(TypeError, match="out_fp16"):
+            binding.read(R, w, Wd, Wu, out=(mixed, good, img))
+    with pytest.raises(TypeError, match="out_bf16"):  # an fp16 tensor is not a bf16 image
+        binding.read(R, w, Wd, Wu, out=(mixed, torch.empty((T, 2560), dtype=torch.float16), good))
