@@ -21,6 +21,8 @@ HC_ERR_ALIGN = 2
 HC_ERR_DEVICE = 3
 HC_ERR_NOMEM = 4
 HC_ERR_LAUNCH = 5
+HC_ERR_SIZE = 6
+HC_ERR_STATE = 7
 
 # Every function the header exports, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -28,6 +30,7 @@ SIGNATURES = {
     "hc_read": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_read_commit": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_read_bf16_lo": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hc_read_noalloc": (ctypes.c_int, [ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hc_short_window_on": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)]),
     "hc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hc_last_hip_error": (ctypes.c_int, []),
@@ -105,6 +108,16 @@ def hc_read_bf16_lo(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, ou
 
     Returns the status code (0 = HC_OK)."""
     return library().hc_read_bf16_lo(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
+                                     _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
+                                     _stream(stream))
+
+
+def hc_read_noalloc(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, stream=None):
+    """hc_read_noalloc of the C ABI: hc_read for T <= 32 without any device
+    allocation (after hc_short_window_on() on the device).
+
+    Returns the status code (0 = HC_OK)."""
+    return library().hc_read_noalloc(int(T), _ptr(R), _ptr(pending), _ptr(w_norm), _ptr(W_down),
                                      _ptr(W_up), _ptr(out_mixed), _ptr(out_bf16), _ptr(out_fp16),
                                      _stream(stream))
 

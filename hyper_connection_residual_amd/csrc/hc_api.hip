@@ -314,10 +314,24 @@ int short_window_on(int dev, Workspace* ws, bool* on)
         *on = it->second;
         return HC_OK;
     }
-    char why[160] = "";
+    char why[200] = "";
     const int st = run_short_window_check(dev, ws, on, why, sizeof why);
     if (st != HC_OK)
         return st;
+    if (*on) {
+        // set-up of the allocation-free reads on this device: the address of
+        // their static scratch (cleared) and the cross-stream order's event,
+        // so that hc_read_noalloc never allocates
+        hipError_t e = hc::noalloc_setup(dev, ws->stream);
+        if (e != hipSuccess)
+            return record(e, HC_ERR_DEVICE);
+        std::lock_guard<std::mutex> lock(g_mutex);
+        ShortOrder& so = g_short_order[dev];
+        if (!so.done && (e = hipEventCreateWithFlags(&so.done, hipEventDisableTiming)) != hipSuccess) {
+            so.done = nullptr;
+            return record(e, HC_ERR_DEVICE);
+        }
+    }
     g_short_window.emplace(dev, *on);
     if (log_enabled())
         std::fprintf(stderr, "hc: device %d: the short-window read is %s (start-up check: %s)%s\n", dev,
@@ -441,6 +455,38 @@ HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, cons
     return read_impl(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, nullptr, stream, true);
 }
 
+HC_API int hc_read_noalloc(int64_t T, const float* R, const float* pending, const float* w_norm,
+                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                           uint16_t* out_bf16, uint16_t* out_fp16, void* stream)
+{
+    if (T < 1 || !R || !w_norm || !W_down || !W_up || !out_mixed || !out_bf16 || !out_fp16)
+        return HC_ERR_ARG;
+    if (T > hc::kDecMaxT)
+        return HC_ERR_SIZE;
+    if (!aligned16(R) || (pending && !aligned16(pending)) || !aligned16(w_norm) ||
+        !aligned16(W_down) || !aligned16(W_up) || !aligned16(out_mixed) ||
+        !aligned16(out_bf16) || !aligned16(out_fp16))
+        return HC_ERR_ALIGN;
+    int dev = 0;
+    int st = current_device(&dev);
+    if (st != HC_OK)
+        return st;
+    {
+        // set up by the device's start-up check, which must have kept the
+        // short-window kernel (the wide path needs allocated scratch)
+        std::lock_guard<std::mutex> lock(g_check_mutex);
+        auto it = g_short_window.find(dev);
+        if (it == g_short_window.end() || !it->second)
+            return HC_ERR_STATE;
+    }
+    hc::DecodeScratch scr;
+    if (!hc::noalloc_scratch(dev, &scr))
+        return HC_ERR_STATE;
+    const hipError_t e = launch_short_window(dev, static_cast<hipStream_t>(stream), static_cast<int>(T), R, pending,
+                                             w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, nullptr, scr);
+    return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);
+}
+
 HC_API int hc_short_window_on(int* on)
 {
     if (!on)
@@ -471,6 +517,9 @@ HC_API const char* hc_status_string(int status)
     case HC_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU or could not be queried";
     case HC_ERR_NOMEM: return "the scratch workspace could not be allocated (or the first call on a stream was under graph capture)";
     case HC_ERR_LAUNCH: return "a kernel launch failed";
+    case HC_ERR_SIZE: return "T is above 32, the most hc_read_noalloc takes";
+    case HC_ERR_STATE: return "allocation-free reads are not set up on this device (call hc_short_window_on first, "
+                              "outside graph capture; they need the short-window kernel on)";
     default: return "unknown status";
     }
 }
@@ -502,23 +551,29 @@ HC_API int hc_timeouts(void* stream, uint32_t* count)
     if (e != hipSuccess)
         return record(e, HC_ERR_DEVICE);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    Workspace* ws = nullptr;
+    uint32_t* counters[2] = {nullptr, nullptr};
     {
         std::lock_guard<std::mutex> lock(g_mutex);
         auto it = g_workspaces.find(std::make_pair(dev, stream_key(hs)));
-        if (it == g_workspaces.end())
-            return HC_OK;
-        ws = it->second;
+        if (it != g_workspaces.end())
+            counters[0] = it->second->dec.timeouts;
     }
-    uint32_t v = 0;
-    e = hipMemcpyAsync(&v, ws->dec.timeouts, sizeof(v), hipMemcpyDeviceToHost, hs);
-    if (e == hipSuccess)
-        e = hipMemsetAsync(ws->dec.timeouts, 0, sizeof(uint32_t), hs);
+    hc::DecodeScratch na;
+    if (hc::noalloc_scratch(dev, &na))
+        counters[1] = na.timeouts;  // the allocation-free reads of this device
+    uint32_t v[2] = {0, 0};
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+        if (!counters[i])
+            continue;
+        e = hipMemcpyAsync(&v[i], counters[i], sizeof(uint32_t), hipMemcpyDeviceToHost, hs);
+        if (e == hipSuccess)
+            e = hipMemsetAsync(counters[i], 0, sizeof(uint32_t), hs);
+    }
     if (e == hipSuccess)
         e = hipStreamSynchronize(hs);
     if (e != hipSuccess)
         return record(e, HC_ERR_DEVICE);
-    *count = v;
+    *count = v[0] + v[1];
     return HC_OK;
 }
 

@@ -966,11 +966,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         __hip_atomic_store(&s.gen[b], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The allocation-free reads' scratch: one short-window workspace in a
+// file-scope device array, which every GPU the library runs on holds until
+// the process ends.  Host code never uses its name as an address: set-up takes
+// each device's own address of it with hipGetSymbolAddress.
+constexpr size_t kScratchWords = kPartWords + kSsqWords + kLoWords + (kDecWGs + 64) / 2;
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+constexpr int kMaxDevices = 64;
+void* g_noalloc_base[kMaxDevices] = {};  // per device: the array's address (set-up done)
+
 }  // namespace
 
 size_t decode_scratch_bytes()
 {
     return sizeof(uint64_t) * (kPartWords + kSsqWords + kLoWords) + sizeof(uint32_t) * (kDecWGs + 64);
+}
+
+hipError_t noalloc_setup(int dev, hipStream_t stream)
+{
+    static_assert(sizeof(scratch) >= sizeof(uint64_t) * (kPartWords + kSsqWords + kLoWords) +
+                                           sizeof(uint32_t) * (kDecWGs + 64), "scratch size");
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    if (g_noalloc_base[dev])
+        return hipSuccess;
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return e;
+    // the hand-off protocol needs every word and counter to start at zero
+    e = hipMemsetAsync(p, 0, decode_scratch_bytes(), stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return e;
+    g_noalloc_base[dev] = p;
+    return hipSuccess;
+}
+
+bool noalloc_scratch(int dev, DecodeScratch* s)
+{
+    if (dev < 0 || dev >= kMaxDevices || !g_noalloc_base[dev])
+        return false;
+    decode_scratch_carve(g_noalloc_base[dev], s);
+    return true;
 }
 
 void decode_scratch_carve(void* base, DecodeScratch* s)

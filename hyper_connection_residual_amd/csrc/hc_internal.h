@@ -52,6 +52,13 @@ struct DecodeScratch {
 size_t decode_scratch_bytes();
 void decode_scratch_carve(void* base, DecodeScratch* s);
 
+// Allocation-free reads: set-up (once per device, with that device current,
+// outside graph capture) takes the device's address of a file-scope device
+// array holding one short-window workspace and clears it on `stream`;
+// noalloc_scratch then carves that workspace (false before set-up).
+hipError_t noalloc_setup(int dev, hipStream_t stream);
+bool noalloc_scratch(int dev, DecodeScratch* s);
+
 // Workgroups of the short-window kernel that fit on one CU at once.
 hipError_t decode_resident_blocks(int* blocks_per_cu);
 

@@ -89,6 +89,8 @@ extern "C" {
 #define HC_ERR_DEVICE 3  /* the current device is not gfx950, or a HIP query failed */
 #define HC_ERR_NOMEM 4   /* the scratch workspace could not be allocated */
 #define HC_ERR_LAUNCH 5  /* a kernel launch failed (see hc_last_hip_error) */
+#define HC_ERR_SIZE 6    /* T above 32 for hc_read_noalloc */
+#define HC_ERR_STATE 7   /* hc_read_noalloc before its set-up on the device */
 
 /* Dimensions of the read. */
 #define HC_STREAMS 4
@@ -164,6 +166,31 @@ HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, cons
                     uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
 
 /*
+ * hc_read_noalloc -- hc_read for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It never calls hipMalloc, hipFree or any other allocating
+ * routine: the hand-off scratch of the short-window kernel lives in a
+ * file-scope device array of 3.7 MB that each GPU the library runs on holds
+ * until the process ends, and every allocation-free read of a device shares
+ * it.  Arguments, layouts and results are hc_read's (the same kernel, the
+ * same bits); the caller still passes inputs and outputs.
+ *
+ * Limit: T <= 32 (one short-window launch); a larger T returns HC_ERR_SIZE
+ * and enqueues nothing.  Set-up: the device's start-up check (the first
+ * hc_short_window_on or read on the device, outside graph capture) takes the
+ * array's address, clears it and creates the ordering event; before that, or
+ * where the check turned the short-window kernel off, the call returns
+ * HC_ERR_STATE.  Allocation-free reads are ordered across streams like
+ * short-window reads; replays of captured graphs that hold them must not
+ * overlap on one GPU (they would race on the shared array).  The array keeps
+ * the last call's contents.  Errors as for hc_read, plus HC_ERR_SIZE and
+ * HC_ERR_STATE; expired waits are counted by hc_timeouts on any stream.
+ */
+HC_API int hc_read_noalloc(int64_t T, const float* R, const float* pending, const float* w_norm,
+                           const uint16_t* W_down, const uint16_t* W_up, float* out_mixed,
+                           uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
+
+/*
  * hc_short_window_on -- *on = 1 if the current device reads windows of up to
  * 32 tokens with the short-window kernel, 0 if they take the wide path.  The
  * kernel's hand-offs need its 256 workgroups resident together and placed on
@@ -195,8 +222,9 @@ HC_API void hc_dims(int* n, int* C, int* r, float* eps);
 
 /*
  * hc_timeouts -- number of expired bounded waits recorded in the workspace of
- * (current device, stream) since the last call, then resets it to zero (the
- * reads concerned stored NaN outputs; see Errors above).
+ * (current device, stream) and by the current device's allocation-free reads
+ * since the last call, then resets them to zero (the reads concerned stored
+ * NaN outputs; see Errors above).
  * Synchronizes `stream`.  *count receives 0 when the stream has no workspace.
  * Returns HC_OK or an HC_ERR_* code.
  */

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == ["hc_read", "hc_read_commit", "hc_read_bf16_lo", "hc_short_window_on", "hc_status_string",
+    assert names == ["hc_read", "hc_read_commit", "hc_read_bf16_lo", "hc_read_noalloc", "hc_short_window_on",
+                     "hc_status_string",
                      "hc_last_hip_error", "hc_dims", "hc_timeouts", "hc_stream_read", "hc_release_stream", "hc_release"]
 
 
@@ -58,12 +59,12 @@ def test_dims(lib):
 
 def test_status_strings(lib):
     from hyper_connection_residual_amd import binding
-    texts = {binding.hc_status_string(s) for s in range(6)}
-    assert len(texts) == 6 and all(texts)
+    texts = {binding.hc_status_string(s) for s in range(8)}
+    assert len(texts) == 8 and all(texts) and "unknown status" not in texts
     assert binding.hc_status_string(99) == "unknown status"
 
 
-@pytest.mark.parametrize("entry", ["hc_read", "hc_read_commit", "hc_read_bf16_lo"])
+@pytest.mark.parametrize("entry", ["hc_read", "hc_read_commit", "hc_read_bf16_lo", "hc_read_noalloc"])
 def test_argument_checks_happen_before_any_hip_call(lib, entry):
     from hyper_connection_residual_amd import binding
     fn = getattr(binding, entry)
@@ -100,7 +101,7 @@ def test_stream_read_checks_arguments_first(lib):
 def test_no_device_is_an_error_not_a_fallback(lib):
     from hyper_connection_residual_amd import binding
     good = 0x10000
-    for fn in (binding.hc_read, binding.hc_read_commit, binding.hc_read_bf16_lo):
+    for fn in (binding.hc_read, binding.hc_read_commit, binding.hc_read_bf16_lo, binding.hc_read_noalloc):
         st = fn(1, good, good, good, good, good, good, good, good, 0)
         assert st == binding.HC_ERR_DEVICE
     with pytest.raises(binding.HCError):
@@ -142,3 +143,10 @@ def test_python_read_refuses_image_buffers_of_the_wrong_width(lib):
             binding.read(R, w, Wd, Wu, out=(mixed, good, img))
     with pytest.raises(TypeError, match="out_bf16"):  # an fp16 tensor is not a bf16 image
         binding.read(R, w, Wd, Wu, out=(mixed, torch.empty((T, 2560), dtype=torch.float16), good))
+
+
+def test_noalloc_rejects_windows_above_32_before_any_hip_call(lib):
+    from hyper_connection_residual_amd import binding
+    good = 0x10000
+    for T in (33, 64, 4096):
+        assert binding.hc_read_noalloc(T, *([good] * 8), 0) == binding.HC_ERR_SIZE
