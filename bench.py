@@ -52,13 +52,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for the baseline")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run 5 plain device copies of 256 MiB (the reference for "
-                         "scaling the HBM byte counters of a profiler run)")
+                    help="also run 5 plain device copies of 256 MiB (a known byte count that checks the "
+                         "HBM byte counters of a profiler run)")
+    ap.add_argument("--light", action="store_true",
+                    help="fewer reads per timing loop (for profiler runs that serialize every dispatch)")
     ap.add_argument("--cpu-cores", type=int, default=0,
                     help="host cores for the all-core oracle leg (0: all, at most 16)")
-    ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_wide_reads_hbm_bytes.md"),
-                    help="summary of the profiler's FETCH_SIZE / WRITE_SIZE runs; its figure is "
-                         "reported only if it was measured on the current kernel source")
+    ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_wide_reads_counters.md"),
+                    help="summary of the profiler's counter runs (rocprof_summary counters); its HBM "
+                         "bytes are reported only if they were measured on the current kernel sources")
     return ap.parse_args()
 
 
@@ -131,6 +133,8 @@ def cpu_baseline(args):
 
 def main():
     args = parse()
+    # reads per timing loop: per-T sweep, windows, commit, prefill
+    n_per_T, n_win, n_commit = (24, 24, 8) if args.light else (300, 96, 96)
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the read has no cross-GPU "
               "exchange; see the sharding paragraph of the design notes). Use --gpus 1.",
@@ -192,8 +196,8 @@ def main():
     for T in TS:
         for m in range(10):
             read_on(T, m, stream)
-        ms = time_region(stream, lambda k, T=T: read_on(T, k % N_SETS, stream), 300)
-        us_eager[str(T)] = round(ms * 1e3 / 300, 3)
+        ms = time_region(stream, lambda k, T=T: read_on(T, k % N_SETS, stream), n_per_T)
+        us_eager[str(T)] = round(ms * 1e3 / n_per_T, 3)
     print("# eager us per read by T: %s" % us_eager, file=sys.stderr, flush=True)
 
     # ---- the floor: one launch of the short-window kernel's shape that only
@@ -209,8 +213,8 @@ def main():
 
     for k in range(N_SETS):
         stream_once(k)
-    ms_floor = time_region(stream, stream_once, 300)
-    floor_us = round(ms_floor * 1e3 / 300, 3)
+    ms_floor = time_region(stream, stream_once, n_per_T)
+    floor_us = round(ms_floor * 1e3 / n_per_T, 3)
     print("# stream floor: %.3f us per launch (%.0f GB/s)" % (floor_us, WEIGHT_BYTES / (floor_us * 1e-6) / 1e9),
           file=sys.stderr, flush=True)
     del floor_bufs
@@ -236,8 +240,8 @@ def main():
 
         for k in range(8):
             window_read(k)
-        ms = time_region(stream, window_read, 96)
-        us_windows[str(T)] = round(ms * 1e3 / 96, 3)
+        ms = time_region(stream, window_read, n_win)
+        us_windows[str(T)] = round(ms * 1e3 / n_win, 3)
     print("# windows above 8 tokens, us per read: %s" % us_windows, file=sys.stderr, flush=True)
 
     # ---- the pending write committed by the read (hc_read_commit) against
@@ -262,7 +266,7 @@ def main():
             call(binding.hc_read, k)
             R.add_(P)
 
-        n = 96 if T <= 8 else 10
+        n = n_commit if T <= 8 else (2 if args.light else 10)
         for k in range(4):
             call(binding.hc_read_commit, k)
             read_then_add(k)
@@ -328,11 +332,11 @@ def main():
             w_norm = torch.from_numpy(inp.w_norm).cuda()
             Wd = torch.from_numpy(inp.W_down.view(np.int16)).cuda()
             Wu = torch.from_numpy(inp.W_up.view(np.int16)).cuda()
-            r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 20 if inp.T <= 2048 else 10)
+            r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 2 if args.light else (20 if inp.T <= 2048 else 10))
             prefill_all["T%d" % inp.T] = r
             print("# prefill T=%d: %.4f ms per read" % (inp.T, r["ms_per_read"]), file=sys.stderr, flush=True)
             if inp.T == 8192:  # the bf16-lo mode (hc_read_bf16_lo), its own error-bound contract
-                r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 10, fn=binding.hc_read_bf16_lo)
+                r = time_wide(inp.T, R, None, w_norm, Wd, Wu, 2 if args.light else 10, fn=binding.hc_read_bf16_lo)
                 prefill_all["T8192_bf16_lo"] = r
                 print("# prefill T=8192, bf16 lo: %.4f ms per read" % r["ms_per_read"], file=sys.stderr,
                       flush=True)
@@ -349,7 +353,7 @@ def main():
         R5 = (z / torch.sqrt(chi / 4.0) / np.sqrt(2.0)).contiguous()
         del z, chi
         P5 = (0.05 * torch.randn((T5, 4, 2560), device=dev, generator=g)).contiguous()
-        r = time_wide(T5, R5, P5, w_norm, Wd, Wu, 3)
+        r = time_wide(T5, R5, P5, w_norm, Wd, Wu, 1 if args.light else 3)
         prefill_all["T32768_pending"] = r
         print("# prefill T=32768 with pending: %.4f ms per read" % r["ms_per_read"], file=sys.stderr, flush=True)
         del R5, P5, Wd, Wu

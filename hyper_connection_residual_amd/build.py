@@ -43,10 +43,17 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libhc.so (always recompiles); returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC,
+PROBE_LIB = os.path.join(PKG, "libhc_probe.so")
+
+
+def build(verbose: bool = False, probe: bool = False) -> str:
+    """Compile libhc.so (always recompiles); returns its path.  probe=True
+    builds the timing variant libhc_probe.so instead: the short-window kernel
+    records clock stamps per workgroup (hc_probe_stamps); the library never
+    loads it."""
+    out = PROBE_LIB if probe else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *FLAGS, *(["-DHC_PROBE_STAMPS"] if probe else []), "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -55,9 +62,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, probe="--probe" in sys.argv[1:]))

@@ -60,9 +60,22 @@
 // unrounded product to its partner's rounded one.
 #pragma clang fp contract(off)
 
-// Instrumentation hook: empty in the library; a timing build may define it to
-// record when workgroups pass the numbered points.
-#ifndef HC_PROBE
+// Instrumentation hook: empty in the library.  The timing build (built with
+// HC_PROBE_STAMPS, into a separate library) records, in wave 0 lane 0, the
+// 100 MHz wall clock when the workgroup passes each numbered point, and
+// stores the stamps at the kernel's end into a ring of 64 launches that
+// hc_probe_stamps copies out.  Points: 0 entry, 1 W_down tile and
+// activations landed (y staged), 2 down products done, 3 partial dots
+// stored, 12 hop 1 polls done and 13 lo published (reducers), 14 hop 2 polls
+// done, 7 lo staged, 8 W_up tile landed and lo complete, 9 outputs stored,
+// 15 exit.
+#if defined(HC_PROBE_STAMPS)
+#define HC_PROBE(point, cond)                                       \
+    do {                                                            \
+        if ((cond) && threadIdx.x == 0)                             \
+            probe_t[point] = (unsigned long long)wall_clock64();    \
+    } while (0)
+#elif !defined(HC_PROBE)
 #define HC_PROBE(point, cond) ((void)0)
 #endif
 // Counting hook: empty in the library; a timing build may record how many
@@ -336,6 +349,11 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint4* lds_wave_base)
 // The arguments the first loads need come first: the library is built with
 // kernel-argument preloading, so they arrive in SGPRs and no wave has to fetch
 // them from memory (a fetch that queues behind the other CUs' weight traffic).
+#if defined(HC_PROBE_STAMPS)
+// [64 launches (generation mod 64)][256 workgroups][16 points]: wall-clock stamps
+__device__ unsigned long long hc_probe_ring[64 * kDecWGs * 16];
+#endif
+
 template <int T>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint16_t* __restrict__ W_down, const uint16_t* __restrict__ W_up, const float* R,
@@ -394,6 +412,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // its own r: a producer that ran on another XCD shows up as an expired
     // (counted) wait, never as a silent stale read.
     const uint32_t rot = (__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) - (uint32_t)x) & 7u;
+#if defined(HC_PROBE_STAMPS)
+    unsigned long long probe_t[16] = {};
+#endif
     HC_PROBE(0, threadIdx.x == 0);
     if (threadIdx.x == 0)
         poisoned_wg = 0;  // (ordered before any setter by the barriers B1, Bc1, Bs)
@@ -964,6 +985,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&s.gen[b], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#if defined(HC_PROBE_STAMPS)
+    HC_PROBE(15, true);
+    if (threadIdx.x == 0)
+        for (int p = 0; p < 16; ++p)
+            hc_probe_ring[((gen & 63) * kDecWGs + b) * 16 + p] = probe_t[p];
+#endif
 }
 
 // The allocation-free reads' scratch: one short-window workspace in a
@@ -1020,6 +1047,15 @@ void decode_scratch_carve(void* base, DecodeScratch* s)
     s->gen = reinterpret_cast<uint32_t*>(s->lo + kLoWords);
     s->timeouts = s->gen + kDecWGs;
 }
+
+#if defined(HC_PROBE_STAMPS)
+// Timing build only: copies the stamp ring (64 x 256 x 16 values) to host.
+extern "C" __attribute__((visibility("default"))) int hc_probe_stamps(unsigned long long* host)
+{
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(hc_probe_ring), sizeof(hc_probe_ring), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess ? 0 : 1;
+}
+#endif
 
 hipError_t decode_resident_blocks(int* blocks_per_cu)
 {

@@ -2,20 +2,18 @@
 
     python -m hyper_connection_residual_amd.rocprof_summary stats <kernel_stats.csv> > out.md
     python -m hyper_connection_residual_amd.rocprof_summary trace <kernel_trace.csv> > out.md
-    python -m hyper_connection_residual_amd.rocprof_summary bytes <fetch counter_collection.csv> \
-        <write counter_collection.csv> <fetch run log> <write run log> > out.md
+    python -m hyper_connection_residual_amd.rocprof_summary counters <run log>... -- <counter_collection.csv>... > out.md
 
 `stats` tabulates per-kernel durations; `trace` does the same per (kernel,
-workgroup count), which separates launches of one kernel at different sizes.  `bytes` tabulates HBM bytes per
-dispatch from one FETCH_SIZE run and one WRITE_SIZE run (KiB per dispatch).
-Both counters are scaled by what they read for a plain device-to-device copy of
-known size run in the same process (the runtime's copy kernel, which bench.py
---calib-copy launches: 5 copies of 256 MiB); the scale factors are printed.  The
-short-window kernel's sweep average (T = 1..8) is printed on a line bench.py
-reads, together with the hash of the kernel sources the profiled runs were
-built from, taken from those runs' own output (bench.py prints it; both runs
-must agree), so a later change to the kernels makes bench.py report the
-traffic as unknown.
+workgroup count), which separates launches of one kernel at different sizes.
+`counters` averages every collected counter per dispatch and kernel size and
+derives HBM bytes from the per-size request counters (no calibration factor),
+the matrix cores' busy share and bf16 matrix flops.  It also writes the
+short-window kernel's HBM bytes per launch, averaged over the verify-window
+sweep, on a line bench.py reads, together with the hash of the kernel sources
+the profiled runs were built from, taken from those runs' own output (bench.py
+prints it; every run must agree), so a later change to the kernels makes
+bench.py report the traffic as unknown.
 """
 from __future__ import annotations
 
@@ -28,7 +26,6 @@ import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(_PKG, "csrc")
-COPY_BYTES = 5 * (256 << 20)  # bench.py --calib-copy
 
 
 def source_hash() -> str:
@@ -82,42 +79,6 @@ def trace(path: str) -> str:
     return "\n".join(out)
 
 
-def _per_kernel(path):
-    acc = collections.defaultdict(list)
-    with open(path) as f:
-        for row in csv.DictReader(f):
-            acc[short_name(row["Kernel_Name"])].append(float(row["Counter_Value"]) * 1024.0)
-    return acc
-
-
-def traffic(fetch_path: str, write_path: str, fetch_log: str, write_log: str) -> str:
-    hashes = {hash_in_log(fetch_log), hash_in_log(write_log)}
-    if len(hashes) != 1 or None in hashes:
-        raise SystemExit("the two profiled runs printed different (or no) kernel source hashes: %s" % hashes)
-    run_hash = hashes.pop()
-    fetch, write = _per_kernel(fetch_path), _per_kernel(write_path)
-    copy = "__amd_rocclr_copyBuffer"
-    f_scale = COPY_BYTES / sum(fetch[copy]) if fetch.get(copy) else float("nan")
-    w_scale = COPY_BYTES / sum(write[copy]) if write.get(copy) else float("nan")
-    out = ["copy-kernel calibration: FETCH_SIZE x %.3f, WRITE_SIZE x %.3f "
-           "(%d MiB copied)" % (f_scale, w_scale, COPY_BYTES >> 20), "",
-           "| kernel | dispatches | HBM read MB | HBM write MB |", "|---|---|---|---|"]
-    sweep = []
-    for k in sorted(set(fetch) | set(write)):
-        fr = fetch.get(k, [0.0])
-        wr = write.get(k, [0.0])
-        rd = f_scale * sum(fr) / len(fr)
-        wt = w_scale * sum(wr) / len(wr)
-        out.append("| %s | %d | %.3f | %.3f |" % (k, len(fr), rd / 1e6, wt / 1e6))
-        m = re.match(r"hc::decode_kernel<(\d+)>", k)
-        if m and 1 <= int(m.group(1)) <= 8:  # the verify-window sweep's instances
-            sweep.append(rd + wt)
-    if sweep:
-        out += ["", "short-window kernel HBM bytes per launch (sweep average): %d" % round(sum(sweep) / len(sweep)),
-                "short-window kernel source hash: %s" % run_hash]
-    return "\n".join(out)
-
-
 def read_traffic(md_path: str):
     """(bytes per launch, source hash) from a `bytes` summary, or None."""
     if not os.path.exists(md_path):
@@ -134,12 +95,73 @@ def read_traffic(md_path: str):
     return (val, h) if val is not None else None
 
 
+def _counter_rows(paths):
+    """{(kernel, workgroups): {counter: [value per dispatch]}} over counter runs."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                wgs = int(row["Grid_Size"]) // max(1, int(row["Workgroup_Size"]))
+                acc[(short_name(row["Kernel_Name"]), wgs)][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    return acc
+
+
+def counters(log_paths, csv_paths, kernels=r"hc::|copyBuffer") -> str:
+    """Per (kernel, workgroup count): every collected counter averaged per
+    dispatch, and the figures derived from them: HBM bytes from the per-size
+    request counters (32 / 64 / 128-byte reads, 32 / 64-byte writes: no
+    calibration factor), MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES, summed over
+    the 1024 SIMDs, over SQ_BUSY_CYCLES, summed over the 32 shader engines of
+    32 SIMDs each) and bf16 matrix flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512).
+    The short-window kernel's HBM bytes per launch, averaged over the
+    verify-window sweep (T = 1..8), go on a line bench.py reads, with the
+    kernel-source hash that every profiled run printed (they must agree)."""
+    hashes = {hash_in_log(p) for p in log_paths}
+    if len(hashes) != 1 or None in hashes:
+        raise SystemExit("the profiled runs printed different (or no) kernel source hashes: %s" % hashes)
+    run_hash = hashes.pop()
+    acc = _counter_rows(csv_paths)
+    names = sorted({c for v in acc.values() for c in v})
+    sweep = []
+    out = ["counters taken on kernel source hash %s" % run_hash, "",
+           "| kernel | workgroups | dispatches | " + " | ".join(names) + " | derived |",
+           "|---|---|---|" + "---|" * len(names) + "---|"]
+    for (k, wgs), cs in sorted(acc.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        if not re.search(kernels, k):
+            continue
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        der = []
+        rd = None
+        if all(c in mean for c in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")):
+            rd = 32 * mean["TCC_EA0_RDREQ_32B_sum"] + 64 * mean["TCC_EA0_RDREQ_64B_sum"] + \
+                128 * mean["TCC_EA0_RDREQ_128B_sum"]
+            der.append("read %.3f MB" % (rd / 1e6))
+        if all(c in mean for c in ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")):
+            wr = 64 * mean["TCC_EA0_WRREQ_64B_sum"] + 32 * (mean["TCC_EA0_WRREQ_sum"] - mean["TCC_EA0_WRREQ_64B_sum"])
+            der.append("written %.3f MB" % (wr / 1e6))
+            mm = re.match(r"hc::decode_kernel<(\d+)>", k)
+            if mm and 1 <= int(mm.group(1)) <= 8 and rd is not None:
+                sweep.append(rd + wr)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("SQ_BUSY_CYCLES", 0) > 0:
+            der.append("MFMA busy %.1f %%" % (100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (32 * mean["SQ_BUSY_CYCLES"])))
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+            der.append("bf16 MFMA %.2f GFLOP" % (512 * mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / 1e9))
+        out.append("| %s | %d | %d | " % (k, wgs, n) + " | ".join(
+            ("%.4g" % mean[c]) if c in mean else "" for c in names) + " | " + "; ".join(der) + " |")
+    if sweep:
+        out += ["", "short-window kernel HBM bytes per launch (sweep average): %d" % round(sum(sweep) / len(sweep)),
+                "short-window kernel source hash: %s" % run_hash]
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
     elif sys.argv[1] == "trace":
         print(trace(sys.argv[2]))
-    elif sys.argv[1] == "bytes":
-        print(traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5]))
+    elif sys.argv[1] == "counters":  # counters <log>... -- <csv>...
+        cut = sys.argv.index("--")
+        print(counters(sys.argv[2:cut], sys.argv[cut + 1:]))
     else:
         raise SystemExit(__doc__)

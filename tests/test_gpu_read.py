@@ -268,7 +268,7 @@ def test_lo_is_at_fp32_level(T, pending):
     assert np.max(rel) <= LO_TOL
 
 
-@pytest.mark.parametrize("T, pending", [(100, False), (300, False), (4097, True)])
+@pytest.mark.parametrize("T, pending", [(100, False), (300, False), (2048, False), (4097, True)])
 def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     """hc_read_bf16_lo, stage-wise: the oracle's mode that rounds its exact lo
     to bf16 (nearest even) before the up projection is the reference, held to
@@ -281,14 +281,15 @@ def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     rounding its flagged values the other way could move one of its mixed
     values by more than 1e-6 of max|mixed| (half the tolerance).  The expected
     values are the oracle's alone; the test prints how many tokens it leaves
-    out.  T = 100: 16-column up+mix tiles without pending; T = 300: 64-column
-    tiles; T = 4097 (two chunks, with pending): a sample of tokens.  The mode
+    out.  T = 100: 16-column up+mix tiles without pending; T = 300 and 2048:
+    the persistent up+mix; T = 4097 (two chunks, with pending): the
+    per-tile up+mix, a sample of tokens.  The mode
     must also differ from the exact read (the fast path ran)."""
     _case("bf16-lo mode against the oracle fed bf16(lo): T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(5 if pending else 3, T=T, seed=T + 1)
     gpu = hip_read(to_device(inp), bf16_lo=True)
-    toks = np.arange(T) if T <= 300 else np.array(sorted(set(_sample_tokens(T, k=40, seed=T).tolist()) |
-                                                        {0, 4095, 4096}))
+    toks = np.arange(T) if T <= 300 else np.array(sorted(set(_sample_tokens(T, k=64, seed=T).tolist()) |
+                                                        {0, T - 1} | ({4095, 4096} if T > 4096 else set())))
     R = inp.R[toks]
     P = None if inp.pending is None else inp.pending[toks]
     ref, lo = orc.oracle_read(R, inp.w_norm, inp.W_down, inp.W_up, P, eps=inp.eps, threads=THREADS,
