@@ -78,7 +78,7 @@ hipError_t launch_decode(int T, const float* R, const float* P, const float* w_n
 // Wide path (T > kDecMaxT): three launches per chunk of up to kPrefillChunk
 // tokens (down partials, lo planes, up projection with the mix epilogue).
 // ---------------------------------------------------------------------------
-constexpr int kPrefillChunk = 4096;
+constexpr int kPrefillChunk = 8192;
 
 size_t prefill_scratch_bytes(int chunk);
 

@@ -5,12 +5,13 @@
 // finer" with the norm folded into the down projection ("#2488 sycl/A770",
 // Summary item 4) and the up projection fused with gr_mix_r as in "#1370
 // prefill: ... gr_mix_r as its epilogue", "What it does": gated (T x 10240
-// fp32) never leaves registers.  Three launches per chunk of up to 4096 tokens:
+// fp32) never leaves registers.  Three launches per chunk of up to 8192 tokens:
 //
 //   P1 down:  part[sig][t][j] = sum_{k in split sig} W_down[j][k] * (R'[t][k] *
 //             w_norm[k]) and ssq[sig][t] = sum_{k in sig} R'[t][k]^2 over S
-//             column splits that lie inside the streams: S = 8 (stream
-//             halves, 1280 columns) for 4096-token chunks, 16 (quarters) for
+//             column splits that lie inside the streams: S = 4 (whole streams)
+//             for chunks of more than 8064 tokens without pending, 8 (stream
+//             halves, 1280 columns) from 3969 tokens, 16 (quarters) for
 //             chunks of 1025..3968 tokens, 32 (320 columns) for 385..1024 and
 //             80 (128 columns) up to 384 tokens (splits_for).
 //   P2 lo:    rs[t][s] = 1/sqrt(sum of stream s's split ssq / 2560 + eps) and
@@ -300,10 +301,11 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
         // steps later); with 2 slots it is converted at the next step and every
         // wait drains.
         issue_w(0);
-        if (64 * pw + lane < SW / 4)  // the split's w_norm: SW / 4 chunks, at most 8 wave instructions
-            dma16(w_norm + kbase + 4 * (64 * pw + lane), lds + kNormOff + 64 * pw);
-        if (64 * (pw + 4) + lane < SW / 4)
-            dma16(w_norm + kbase + 4 * (64 * (pw + 4) + lane), lds + kNormOff + 64 * (pw + 4));
+        // the split's w_norm: SW / 4 chunks, wave instructions pw, pw + 4, ..
+#pragma unroll
+        for (int k = 0; k < (SW / 4 + 255) / 256; ++k)
+            if (64 * (pw + 4 * k) + lane < SW / 4)
+                dma16(w_norm + kbase + 4 * (64 * (pw + 4 * k) + lane), lds + kNormOff + 64 * (pw + 4 * k));
 #pragma unroll
         for (int k = 0; k < RS - 1; ++k)
             issue_raw(k);
@@ -798,16 +800,20 @@ int tiles_of(int tokens)
 }
 
 // P1's split count.  A workgroup takes a whole CU (its LDS), so the grid
-// should fill the chip once: chunks of 4096 tokens (32 tiles) use stream
-// halves, longer-than-1024-token chunks stream quarters (as before: 144-496
-// workgroups); shorter chunks split K finer so that short reads still stream
-// W_down over most of the chip: 32 splits (320 columns) for 4-8 tiles, 80
-// splits (128 columns, the narrowest the ring takes: 4 K steps) for 1-3
-// tiles.  The partial array never holds more than 16 x 3968 (split, token)
-// slots.
-int splits_for(int tokens)
+// should fill the chip once: chunks of 64 tiles (8192 tokens) without a
+// pending write use whole streams (4 splits; with pending the raw slots of
+// 2560-column splits do not fit in LDS), chunks of 32 tiles or more stream
+// halves, longer-than-1024-token chunks stream quarters (144-496 workgroups);
+// shorter chunks split K finer so that short reads still stream W_down over
+// most of the chip: 32 splits (320 columns) for 4-8 tiles, 80 splits (128
+// columns, the narrowest the ring takes: 4 K steps) for 1-3 tiles.  Fewer
+// splits write and read fewer partials (4 x 8192 x 320 floats, 42 MB, for an
+// 8192-token chunk against 84 MB as two chunks of stream halves).
+int splits_for(int tokens, bool pending)
 {
     const int tiles = (tokens + kDnTok - 1) / kDnTok;
+    if (!pending && tiles * 4 >= 256)
+        return 4;
     if (tiles * 8 >= 256)
         return 8;
     if (tiles > 8)
@@ -818,29 +824,40 @@ int splits_for(int tokens)
 }
 
 template <int S>
-void launch_down_lo(int Tc, int tiles, const float* Rc, const float* Pc, const float* w_norm,
-                    const uint16_t* W_down, float* part, float* ssq, uint4* planes, hipStream_t stream)
+void launch_lo(int Tc, int tiles, float* part, float* ssq, uint4* planes, hipStream_t stream)
 {
-    const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
-    if (Pc)
-        hipLaunchKernelGGL((prefill_down<S, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
-    else
-        hipLaunchKernelGGL((prefill_down<S, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
     const int items = tiles * kTok * (kRank / 4);
     constexpr int lanes = S >= 32 ? 4 : 1;  // lanes per item (as in prefill_lo)
     hipLaunchKernelGGL(prefill_lo<S>, dim3((lanes * items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part,
                        ssq, planes);
 }
 
+template <int S>
+void launch_down_lo(int Tc, int tiles, const float* Rc, const float* Pc, const float* w_norm,
+                    const uint16_t* W_down, float* part, float* ssq, uint4* planes, hipStream_t stream)
+{
+    const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
+    if constexpr (S >= 8) {  // (4 splits are never used with pending)
+        if (Pc) {
+            hipLaunchKernelGGL((prefill_down<S, true>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part,
+                               ssq);
+            return launch_lo<S>(Tc, tiles, part, ssq, planes, stream);
+        }
+    }
+    hipLaunchKernelGGL((prefill_down<S, false>), grid1, block1, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+    launch_lo<S>(Tc, tiles, part, ssq, planes, stream);
+}
+
 // (split, token) slots of the partial array, enough for any chunk of up to
-// `chunk` tokens
+// `chunk` tokens, with or without pending
 size_t part_slots(int chunk)
 {
     size_t most = 0;
-    for (int tc = chunk; tc > 0; tc -= kDnTok) {  // splits_for changes only at tile boundaries
-        const size_t n = (size_t)splits_for(tc) * tc;
-        most = most > n ? most : n;
-    }
+    for (int tc = chunk; tc > 0; tc -= kDnTok)  // splits_for changes only at tile boundaries
+        for (int pending = 0; pending < 2; ++pending) {
+            const size_t n = (size_t)splits_for(tc, pending != 0) * tc;
+            most = most > n ? most : n;
+        }
     return most;
 }
 
@@ -868,7 +885,8 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         const float* Rc = R + in_off;
         const float* Pc = P ? P + in_off : nullptr;
         const int tiles = tiles_of(Tc);
-        switch (splits_for(Tc)) {
+        switch (splits_for(Tc, Pc != nullptr)) {
+        case 4: launch_down_lo<4>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
         case 8: launch_down_lo<8>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
         case 16: launch_down_lo<16>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;
         case 32: launch_down_lo<32>(Tc, tiles, Rc, Pc, w_norm, W_down, part, ssq, planes, stream); break;

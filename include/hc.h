@@ -32,7 +32,7 @@
  * stream).  No host synchronization; results are visible to later work on the
  * same stream.  The library keeps a scratch workspace per (device, stream):
  * 3.7 MB for the short-window kernel, allocated on the first call on that
- * stream, and a fixed 87 MB for the wide path, allocated on the stream's
+ * stream, and a fixed 95 MB for the wide path, allocated on the stream's
  * first wide read; later calls allocate nothing.  Workspaces are found by
  * the stream's handle value: call hc_release_stream before destroying a
  * stream that ran reads (otherwise its workspace lives until hc_release, and

@@ -132,12 +132,12 @@ def test_window_equals_its_halves(T, half):
 
 
 @pytest.mark.parametrize("T, pending", [(1, True), (5, True), (8, False), (16, True), (24, True), (300, True),
-                                        (4097, True)])
+                                        (8193, True)])
 def test_commit_writes_the_pending_update(T, pending):
     """hc_read_commit: the outputs are hc_read's, bit for bit, and R then holds
     the oracle's committed residual fl32(R + pending), bit for bit (untouched
     without a pending write).  Covers the short-window kernel at 1, 2, 3 and 6
-    MFMA chains, and the wide path over two chunks."""
+    MFMA chains, and the wide path over two chunks (8192 + 1 tokens)."""
     _case("commit: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=2) if T <= 24 else wl.config_inputs(5, T=T, seed=T)
     if not pending:
@@ -450,21 +450,24 @@ def test_full_size_config5_every_tile():
 
 @pytest.mark.parametrize("T, pending", [(128, False), (129, True), (256, True), (257, False), (384, False),
                                         (385, True), (700, False), (1024, True), (1025, False), (2000, True),
-                                        (3968, False), (3969, True), (4097, False), (4097, True)])
+                                        (3968, False), (3969, True), (4097, False), (8064, False), (8065, False),
+                                        (8192, True), (8193, False)])
 def test_wide_path_boundaries(T, pending):
     """Token counts at the wide path's internal boundaries: one token past a
     128-token down tile; the up+mix tile changes from 16 to 64 columns after
     256 tokens (4 token tiles); the down projection's K-split count changes
     from 80 (128-column splits) to 32 after 384 tokens, to 16 (stream
-    quarters) after 1024 and to 8 (stream halves) after 3968; one token past a
-    4096-token chunk (the second chunk holds a single token).  700 and 2000
-    run the 32- and 16-split down projections with and without pending, so
-    that every instance a valid call reaches runs.  Oracle on the tokens
-    around each boundary plus a random sample."""
+    quarters) after 1024, to 8 (stream halves) after 3968 and, without
+    pending, to 4 (whole streams) after 8064; one token past an 8192-token
+    chunk (the second chunk holds a single token).  700 and 2000 run the 32-
+    and 16-split down projections with and without pending, 8192 the 8-split
+    one with pending, so that every instance a valid call reaches runs.
+    Oracle on the tokens around each boundary plus a random sample."""
     _case("wide path boundary: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(5 if pending else 3, T=T, seed=T)
     gpu = hip_read(to_device(inp))
-    edges = {t for b in (64, 127, 128, 129, 256, 384, 1024, 3968, 4095, 4096) for t in (b - 1, b) if 0 <= t < T}
+    edges = {t for b in (64, 127, 128, 129, 256, 384, 1024, 3968, 4095, 4096, 8064, 8191, 8192)
+             for t in (b - 1, b) if 0 <= t < T}
     toks = np.array(sorted(set(_sample_tokens(T, k=24, seed=T).tolist()) | edges))
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="T=%d pending=%s" % (T, pending))
 
