@@ -18,23 +18,27 @@
 //             lo[t][j] = sum_s rs[t][s] * (stream s's split partials), stored
 //             in fp32 in the tiled layout P3 copies into LDS verbatim (P3
 //             splits each value into its three bf16 pieces in registers).
-//   P3 up+mix: a tile of 64 tokens x 64 output columns x 4 streams (16
-//             columns for chunks of at most 256 tokens): the up projection
-//             (K = 320) on the matrix cores, then the mix of the 4 streams with
-//             R' and the bf16 / fp16 images, all in registers.
+//   P3 up+mix: the up projection (K = 320) on the matrix cores, then the mix
+//             of the 4 streams with R' and the bf16 / fp16 images, all in
+//             registers.  Chunks of at most 256 tokens: 16-column tiles
+//             (prefill_upmix).  Longer chunks: 128 tokens x 64 columns x 4
+//             streams per workgroup of 8 waves, persistent over its items
+//             without pending (prefill_upmix3), one item per workgroup with
+//             pending or for a ragged last 128 tokens (prefill_upmix2).
 //
 // gfx950 design:
 // * Both matrix kernels run bf16 v_mfma_f32_16x16x32_bf16 with every fp32
 //   activation split exactly into three bf16 pieces (hi + mid + lo3 == x), so
 //   each product is exact and the result stays fp32-faithful.
 // * Weight operands (and P3's lo tiles, and P1's raw activations) go from
-//   memory straight into LDS (global_load_lds_dwordx4, 16 bytes a lane)
-//   through rings: P1 loads its W_down panel one K step of 32 ahead and raw R
-//   (and pending) two or three steps ahead; P3 runs a three-stage ring two
-//   steps ahead.  LDS is read with inline-asm ds_read_b128 and every wait is
-//   explicit: the compiler, seeing an LDS read that may alias a load still
-//   landing in LDS, would wait for ALL loads in flight (vmcnt(0)) and
-//   serialise the ring.
+//   memory straight into LDS (16 bytes a lane, global_load_lds_dwordx4 or
+//   its buffer form) through rings: P1 loads its W_down panel one K step of
+//   32 ahead and raw R (and pending) two or three steps ahead; the 16-column
+//   P3 runs a three-stage ring two steps ahead, the 128-token ones a
+//   five-stage ring four steps ahead.  LDS is read with inline-asm
+//   ds_read_b128 and every wait is explicit: the compiler, seeing an LDS read
+//   that may alias a load still landing in LDS, would wait for ALL loads in
+//   flight (vmcnt(0)) and serialise the ring.
 // * Inside LDS a K step of a weight tile is a "panel": one row per matrix
 //   row, four 16-byte chunks per row, chunk c of row r stored at slot
 //   4 r + (c ^ ((r >> 1) & 3)).  LDS serves a 16-byte read to 8 lanes per
@@ -42,9 +46,8 @@
 //   hit distinct bank groups (measured: the swizzle by r >> 2 instead left
 //   ~45 % of LDS cycles in bank conflicts).
 // * P1 takes a whole CU (12 waves, up to 157 KB of LDS: 8 matrix waves and 4
-//   producer waves that load and convert); P3 uses 4 waves and 72 KB, so two
-//   workgroups share a CU and one's epilogue (memory bound) overlaps the
-//   other's matrix work.
+//   producer waves that load and convert); the 128-token P3 takes a whole CU
+//   too (8 waves, 160 KB), the 16-column one 4 waves and 36 KB.
 // * XCD-aware grids (workgroup b runs on XCD b % 8): with 8 splits P1's XCD x
 //   owns split x, so its 820 KB W_down slice stays in that XCD's L2; P3's XCD
 //   x owns 5 of the 40 column groups (W_up slices, 820 KB) and walks the token
@@ -114,6 +117,21 @@ __device__ __forceinline__ void lds_wait(u32x4 (&v)[N])
     for (int i = 0; i < N; ++i)
         asm volatile("" : "+v"(v[i]));
 }
+__device__ __forceinline__ void pin(u32x4& v)
+{
+    asm volatile("" : "+v"(v));
+}
+// Waits until at most N LDS reads of this wave are in flight; the values
+// named are then "produced here", so no use of them moves above the wait,
+// and the scheduler moves no instruction across it.
+template <int N, typename... V>
+__device__ __forceinline__ void lgkm_wait(V&... v)
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+    (pin(v), ...);
+}
 // No memory access moves across this point.
 __device__ __forceinline__ void order()
 {
@@ -125,6 +143,24 @@ template <int VM>
 __device__ __forceinline__ void ring_barrier()
 {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+// The same, leaving the wave's LG most recent LDS reads in flight.
+template <int VM, int LG>
+__device__ __forceinline__ void ring_barrier_lg()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(%1)\n\ts_barrier" ::"n"(VM), "n"(LG) : "memory");
+}
+// A buffer resource over `base` (raw, 2 GB range): loads through it take a
+// 32-bit byte offset per lane and a scalar one.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane through a buffer resource into LDS (lane l's bytes at
+// lds_wave_base + 16 l): the lane's byte offset `voff` and a scalar `soff`.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint4* lds_wave_base, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, soff, 0, 0);
 }
 // 16 bytes per lane from memory into LDS: lane l's bytes land at
 // lds_wave_base + 16 l (the base must be the same for the whole wave).
@@ -510,20 +546,17 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
 }
 
 // ---------------------------------------------------------------------------
-// P3: up projection with the stream mix as its epilogue.  Workgroup b: XCD
-// x = b % 8, q = b / 8: token tile q / 5, column group x + 8 (q % 5) (64
-// columns).  Wave w owns tokens 16 w .. 16 w + 15 of the tile and computes
-// all 64 columns of all 4 streams for them: MFMA A = W_up rows (4 column
-// blocks x 4 streams), B = lo of the wave's tokens, split in registers into
-// its three bf16 pieces.  D then holds, in lane (n, g), token 16 w + n and
-// columns 16 cb + 4 g .. +3 of every stream, so the mix is per lane.
-// LDS stage (24 KB): W_up panel (256 rows: row 64 s + j = W_up row
-// s * 2560 + c0 + j, 16 KB), then the tile's lo block of the step (8 KB).
-// Three stages, loaded two steps ahead.
-// Chunks of at most 4 token tiles use tiles of 16 columns instead (CB = 1
-// column block instead of 4): 160 workgroups per token tile, each streaming
-// a quarter of the W_up panel, so a short read loads W_up over most of the
-// chip instead of 40 CUs.
+// P3 for chunks of at most 4 token tiles: up projection with the stream mix
+// as its epilogue on tiles of 64 tokens x 16 columns x 4 streams, 160
+// workgroups per token tile, each streaming a quarter of a 64-column W_up
+// panel, so a short read loads W_up over most of the chip.  Workgroup b: XCD
+// x = b % 8, q = b / 8: token tile q / 20, column group x + 8 (q % 20).  Wave
+// w owns tokens 16 w .. 16 w + 15 of the tile: MFMA A = W_up rows (4
+// streams), B = lo of the wave's tokens, split in registers into its three
+// bf16 pieces.  D then holds, in lane (n, g), token 16 w + n and columns 4 g
+// .. +3 of every stream, so the mix is per lane.  LDS stage (12 KB): W_up
+// panel (64 rows: row 16 s + j = W_up row s * 2560 + c0 + j, 4 KB), then the
+// tile's lo block of the step (8 KB).  Three stages, loaded two steps ahead.
 // ---------------------------------------------------------------------------
 constexpr int kUpSlots = 3;
 
@@ -537,7 +570,7 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
-template <bool HAS_P, bool BF16_LO, int CB>
+template <bool HAS_P, bool BF16_LO>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* R,
@@ -547,12 +580,12 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                                                         uint16_t* __restrict__ out_fp16,
                                                         float* R_commit)
 {
-    static_assert(CB == 4 || CB == 1, "column blocks");
+    constexpr int CB = 1;                               // column blocks of 16
     constexpr int kCols = 16 * CB;                      // output columns of the tile
-    constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (5 or 20)
-    constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 1024 or 256 chunks
-    constexpr int kUpStage = kUpWChunks + kLoTile;      // 1536 or 768 chunks
-    constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (6 or 3)
+    constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (20)
+    constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 256 chunks
+    constexpr int kUpStage = kUpWChunks + kLoTile;      // 768 chunks
+    constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (3)
     constexpr int NB = 2 * CB;                          // panel blocks of two streams
     __shared__ __align__(16) uint4 lds[kUpSlots * kUpStage];
 
@@ -721,37 +754,255 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                     *reinterpret_cast<float4*>(crow + s * kWidth + 16 * cb) = rv[cb][s];
         }
     }
-    if constexpr (CB == 1) {
-        // 16 columns: lane (n, g) holds token t, columns c0 + 4 g .. +3 of
-        // every stream; the 4 lanes of a token store 64 contiguous bytes
-        const float r[4][4] = {{rv[0][0].x, rv[0][0].y, rv[0][0].z, rv[0][0].w},
-                               {rv[0][1].x, rv[0][1].y, rv[0][1].z, rv[0][1].w},
-                               {rv[0][2].x, rv[0][2].y, rv[0][2].z, rv[0][2].w},
-                               {rv[0][3].x, rv[0][3].y, rv[0][3].z, rv[0][3].w}};
-        float m[4];
+    // 16 columns: lane (n, g) holds token t, columns c0 + 4 g .. +3 of
+    // every stream; the 4 lanes of a token store 64 contiguous bytes
+    const float r[4][4] = {{rv[0][0].x, rv[0][0].y, rv[0][0].z, rv[0][0].w},
+                           {rv[0][1].x, rv[0][1].y, rv[0][1].z, rv[0][1].w},
+                           {rv[0][2].x, rv[0][2].y, rv[0][2].z, rv[0][2].w},
+                           {rv[0][3].x, rv[0][3].y, rv[0][3].z, rv[0][3].w}};
+    float m[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            m[i] = (acc[0][0][i] * r[0][i] + acc[0][1][i] * r[1][i]) + (acc[0][2][i] * r[2][i] + acc[0][3][i] * r[3][i]);
-        if (t < T) {
-            const size_t o = (size_t)t * kWidth + c0 + 4 * g;
-            *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
-            uint32_t bh[4], hh[4];
+    for (int i = 0; i < 4; ++i)
+        m[i] = (acc[0][0][i] * r[0][i] + acc[0][1][i] * r[1][i]) + (acc[0][2][i] * r[2][i] + acc[0][3][i] * r[3][i]);
+    if (t < T) {
+        const size_t o = (size_t)t * kWidth + c0 + 4 * g;
+        *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
+        uint32_t bh[4], hh[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
-                hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
-            }
-            *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
-            *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        for (int i = 0; i < 4; ++i) {
+            bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
+            hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
         }
-        return;
+        *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
+        *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// P3 for chunks of more than 4 token tiles: one workgroup of 8 waves per CU
+// takes 128 tokens (two token tiles) x 64 columns.  Waves 0-3 compute the
+// first token tile, waves 4-7 the second, as above, so each W_up panel in
+// LDS serves 128 tokens.  The ring holds five stages of 32 KB (the W_up
+// panel, then the two tiles' lo blocks) loaded four steps ahead.  A wave
+// reads the lo and the first four W_up operands of step ks + 1 at the end of
+// step ks (stage ks + 1 has landed everywhere by then), so its MFMAs start
+// right after the barrier instead of behind a burst of 8 waves' reads.  The
+// epilogue's R is loaded right after the last stage, four steps before use.
+// ---------------------------------------------------------------------------
+constexpr int kUp2Slots = 5;
+constexpr int kUp2WChunks = 1024;                     // W_up panel of 64 columns x 4 streams
+constexpr int kUp2Stage = kUp2WChunks + 2 * kLoTile;  // 2048 chunks (32 KB)
+constexpr int kUp2Loads = kUp2Stage / 64 / 8;         // wave instructions per stage and wave (4)
+constexpr int kUp2Waves = 8;
+constexpr int kPersistGrid = 256;  // one workgroup per CU
+
+// Loads a wave of prefill_upmix2 has issued after stage `st` by the end of
+// step `step` (issue order: stages 0-3, then per step j stage j + 4 while it
+// exists and two R loads for j < 8); a stage past the last needs no wait.
+constexpr int up2_loads_after(int st, int step)
+{
+    if (st >= kUpSteps)
+        return 16;  // (only R can still be in flight: at most its 16 loads)
+    int n = 0;
+    bool seen = false;
+    for (int k = 0; k < 4; ++k) {  // prologue
+        if (seen)
+            n += kUp2Loads;
+        if (k == st)
+            seen = true;
+    }
+    for (int j = 0; j <= step; ++j) {
+        if (j + 4 < kUpSteps) {
+            if (seen)
+                n += kUp2Loads;
+            if (j + 4 == st)
+                seen = true;
+        }
+        if (j < 8 && seen)
+            n += 2;
+    }
+    return n;
+}
+
+template <bool HAS_P, bool BF16_LO>
+__global__ __launch_bounds__(kUp2Waves * 64, 1) void prefill_upmix2(int T, int tiles, const uint4* __restrict__ lo_tiled,
+                                                                    const uint16_t* __restrict__ W_up,
+                                                                    const float* R,
+                                                                    const float* __restrict__ P,
+                                                                    float* __restrict__ out_mixed,
+                                                                    uint16_t* __restrict__ out_bf16,
+                                                                    uint16_t* __restrict__ out_fp16,
+                                                                    float* R_commit)
+{
+    static_assert(kUpSteps == 10, "schedule");
+    static_assert(kUp2Slots * kUp2Stage * 16 <= 160 * 1024, "LDS");
+    __shared__ __align__(16) uint4 lds[kUp2Slots * kUp2Stage];
+
+    const int b = blockIdx.x;
+    const int x = b & 7, q = b >> 3;
+    const int pair = q / kGroupsPerXcd;
+    const int cg = x + 8 * (q - pair * kGroupsPerXcd);
+    const int t0 = pair * 2 * kTok, c0 = cg * kUpCols;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int hf = wave >> 2, wl = wave & 3;  // token tile of the pair, wave within it
+
+    // stage loads: W_up panel instruction i (0..15) fills rows 16 i .. +15
+    // (lane l: row 16 i + l / 4, chunk (l & 3) ^ ((row >> 1) & 3)), wave w
+    // issues i = w and w + 8; lo: wave w copies 1 KB w of each tile's block
+    // (a second tile past the chunk re-reads the first: its tokens store nothing)
+    const int wchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const uint16_t* wu_lane[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int prow = 16 * (wave + 8 * k) + (lane >> 2);  // panel row = 64 s + j
+        wu_lane[k] = W_up + (size_t)((prow / kUpCols) * kWidth + c0 + (prow % kUpCols)) * kRank + 8 * wchunk;
+    }
+    const int tile1 = 2 * pair + 1 < tiles ? 2 * pair + 1 : 2 * pair;
+    const uint4* lo_lane0 = lo_tiled + (size_t)(2 * pair) * kUpSteps * kLoTile + 64 * wave + lane;
+    const uint4* lo_lane1 = lo_tiled + (size_t)tile1 * kUpSteps * kLoTile + 64 * wave + lane;
+    auto issue = [&](int ks) {
+        uint4* sb = lds + (ks % kUp2Slots) * kUp2Stage;
+        dma16(wu_lane[0] + kKs * ks, sb + 64 * wave);
+        dma16(wu_lane[1] + kKs * ks, sb + 64 * (wave + 8));
+        dma16(lo_lane0 + (size_t)ks * kLoTile, sb + kUp2WChunks + 64 * wave);
+        dma16(lo_lane1 + (size_t)ks * kLoTile, sb + kUp2WChunks + kLoTile + 64 * wave);
+    };
+
+    f32x4_t acc[4][4];  // [column block][stream]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc[cb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint32_t lds0 = lds_addr(lds);
+    // W_up operand of panel block k = 4 s + cb (stream s, column block cb):
+    // this lane's slot in block 0 plus 1 KB per block
+    const uint32_t aoff = 16 * panel_slot(n, g);
+    // lo of token 16 wl + n of the wave's tile, floats 8 g .. 8 g + 7
+    const int lrow = 16 * wl + n;
+    const uint32_t lo_a = 16 * (kUp2WChunks + kLoTile * hf + 8 * lrow + ((2 * g) ^ swz8(lrow)));
+    const uint32_t lo_b = 16 * (kUp2WChunks + kLoTile * hf + 8 * lrow + ((2 * g + 1) ^ swz8(lrow)));
+    // the reads that open step ks: its lo and W_up blocks 0-3
+    auto read_first = [&](int ks, u32x4 (&lv)[2], u32x4 (&w0)[4]) {
+        const uint32_t sb = lds0 + 16 * (ks % kUp2Slots) * kUp2Stage;
+        lv[0] = ds_read16(sb + lo_a);
+        lv[1] = ds_read16(sb + lo_b);
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w0[k] = ds_read16_off<1024 * k>(sb + aoff); });
+    };
+    // step ks with its first reads done by read_first: the other 12 W_up
+    // blocks stream in behind the MFMAs of the earlier ones; an accumulator's
+    // pieces 2, 1, 0 are four MFMAs apart
+    auto compute = [&](int ks, u32x4 (&lv)[2], u32x4 (&w0)[4]) {
+        const uint32_t wb = lds0 + 16 * (ks % kUp2Slots) * kUp2Stage + aoff;
+        u32x4 w1[4], w2[4], w3[4];
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w1[k] = ds_read16_off<1024 * (4 + k)>(wb); });
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w2[k] = ds_read16_off<1024 * (8 + k)>(wb); });
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w3[k] = ds_read16_off<1024 * (12 + k)>(wb); });
+        lgkm_wait<12>(lv[0], lv[1], w0[0], w0[1], w0[2], w0[3]);
+        uint32_t hi[8], mi[8] = {}, l3[8] = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (BF16_LO)  // the fast mode: lo rounded to bf16 (nearest even), one piece
+                hi[e] = __builtin_bit_cast(uint16_t, (__bf16)__uint_as_float(lv[e >> 2][e & 3]));
+            else
+                split3(__uint_as_float(lv[e >> 2][e & 3]), hi[e], mi[e], l3[e]);
+        }
+        u32x4 y[3];
+        y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
+        y[2] = u32x4{l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16)};
+        auto group = [&](int s, u32x4 (&w)[4]) {  // stream s: panel blocks 4 s .. 4 s + 3
+#pragma unroll
+            for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[cb][s] = mfma16(w[cb], y[p], acc[cb][s]);
+        };
+        group(0, w0);
+        lgkm_wait<8>(w1[0], w1[1], w1[2], w1[3]);
+        group(1, w1);
+        lgkm_wait<4>(w2[0], w2[1], w2[2], w2[3]);
+        group(2, w2);
+        lgkm_wait<0>(w3[0], w3[1], w3[2], w3[3]);
+        group(3, w3);
+        __builtin_amdgcn_sched_barrier(0);  // the step's MFMAs issue before the next step's reads
+    };
+
+    // the epilogue's R: this lane's token, columns c0 + 16 cb + 4 g .. +3 of
+    // every stream (tokens past T re-read token T - 1 and store nothing)
+    constexpr int kRLoads = 16;
+    const int t = t0 + kTok * hf + lrow;
+    const int tr = t < T ? t : T - 1;
+    const float* rrow = R + (size_t)tr * kD + c0 + 4 * g;
+    float4 rv[4][4];  // [column block][stream]
+    typedef __attribute__((address_space(1))) const f32x4_t gf32x4;  // global memory
+    gf32x4* rl = (gf32x4*)rrow;  // (loads through it stay between the asm statements)
+    asm volatile("" : "+v"(rl));
+
+    // Step ks issues stage ks + 4, then (steps 0-7) two of the 16 R loads:
+    // issued all at once, R's 128 KB per workgroup would hold up the wave's
+    // instruction stream for thousands of cycles (measured: the step that
+    // issued them took 4-5 times as long as the others).  Loads complete in
+    // issue order; the wait closing step ks needs stage ks + 2 landed, so it
+    // leaves in flight what was issued after that stage.  Step ks ends by
+    // reading step ks + 1's first operands.
+    u32x4 lv[2], w0[4];
+    static_for<0, 4>([&](auto kc) { issue(decltype(kc)::value); });
+    ring_barrier<2 * kUp2Loads>();  // stages 0 and 1 landed everywhere
+    read_first(0, lv, w0);
+    static_for<0, kUpSteps>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 4 < kUpSteps)
+            issue(ks + 4);
+        order();
+        if constexpr (ks < 8) {
+#pragma unroll
+            for (int i = 2 * ks; i < 2 * ks + 2; ++i) {
+                const f32x4_t v = rl[((i & 3) * kWidth + 16 * (i >> 2)) / 4];
+                rv[i >> 2][i & 3] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        order();
+        compute(ks, lv, w0);
+        if constexpr (ks + 1 < kUpSteps) {
+            read_first(ks + 1, lv, w0);
+            ring_barrier_lg<up2_loads_after(ks + 2, ks), 6>();
+        }
+    });
+
+    if (HAS_P) {
+        const float* prow = P + (size_t)tr * kD + c0 + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float4 pv = *reinterpret_cast<const float4*>(prow + s * kWidth + 16 * cb);
+                rv[cb][s].x += pv.x;
+                rv[cb][s].y += pv.y;
+                rv[cb][s].z += pv.z;
+                rv[cb][s].w += pv.w;
+            }
+        // the pending write committed: R' of this lane's token and columns
+        // back into R (no other workgroup reads them in this chunk, and the
+        // down projection of the chunk has finished)
+        if (R_commit && t < T) {
+            float* crow = R_commit + (size_t)t * kD + c0 + 4 * g;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    *reinterpret_cast<float4*>(crow + s * kWidth + 16 * cb) = rv[cb][s];
+        }
     }
     // The wave's 16 tokens x 64 columns of mixed go through 4 KB of LDS of its
-    // own (inside ring slot 1, which the last step does not read) so that
-    // every store instruction writes whole 128-byte lines: written in the MFMA
+    // own (in ring slot 0, which no wave reads after step 5) so that every
+    // store instruction writes whole 128-byte lines: written in the MFMA
     // layout (chunk 4 cb + g of row n at slot (4 cb + g) ^ n), read back as 4
     // rows of 16 lanes x 16 bytes.
-    const uint32_t tb = lds0 + 16 * kUpStage + 4096 * wave;
+    const uint32_t tb = lds0 + 4096 * wave;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
@@ -776,7 +1027,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int row = (lane >> 4) + 4 * k, ch = lane & 15;
-        const int tt = t0 + 16 * wave + row;
+        const int tt = t0 + kTok * hf + 16 * wl + row;
         if (tt < T) {
             const size_t o = (size_t)tt * kWidth + c0 + 4 * ch;
             const float m[4] = {__uint_as_float(mv[k][0]), __uint_as_float(mv[k][1]), __uint_as_float(mv[k][2]),
@@ -792,6 +1043,224 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
             *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// P3 without pending, persistent: one workgroup of 8 waves per CU walks its
+// (128-token pair, 64-column group) items b, b + grid, ...; items are the
+// full token pairs of the chunk (a ragged last pair goes to prefill_upmix2).
+// The stage stream runs on across items: the last four steps of an item
+// load the first four stages of the next (or, after the last item, the
+// current item's again, so every wait counts the same), so a workgroup pays
+// the ring's fill latency once instead of once per item.  Per item the
+// steps are those of prefill_upmix2; the mixed values go through ring slot
+// 4 (stage 9's, free after the item's last step) on their way out.
+// ---------------------------------------------------------------------------
+template <bool BF16_LO>
+__global__ __launch_bounds__(kUp2Waves * 64, 1) void prefill_upmix3(int T, int items, const uint4* __restrict__ lo_tiled,
+                                                                    const uint16_t* __restrict__ W_up,
+                                                                    const float* R,
+                                                                    float* __restrict__ out_mixed,
+                                                                    uint16_t* __restrict__ out_bf16,
+                                                                    uint16_t* __restrict__ out_fp16)
+{
+    static_assert(kUpSteps == 10 && kUp2Slots == 5, "schedule");
+    __shared__ __align__(16) uint4 lds[kUp2Slots * kUp2Stage];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int hf = wave >> 2, wl = wave & 3;
+
+    // stage loads (as in prefill_upmix2): per lane offsets, item bases added per item
+    const int wchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    uint32_t wu_off[2];  // (elements)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int prow = 16 * (wave + 8 * k) + (lane >> 2);  // panel row = 64 s + j
+        wu_off[k] = (uint32_t)((prow / kUpCols) * kWidth + (prow % kUpCols)) * kRank + 8 * wchunk;
+    }
+    const __amdgpu_buffer_rsrc_t rrs = rsrc_of(R);
+    const int lo_off = 64 * wave + lane;
+    struct Item {
+        int t0, c0;  // first token (of the pair) and column
+    };
+    auto item_of = [&](int w) {
+        const int x = w & 7, q = w >> 3;
+        const int pair = q / kGroupsPerXcd;
+        const int cg = x + 8 * (q - pair * kGroupsPerXcd);
+        return Item{pair * 2 * kTok, cg * kUpCols};
+    };
+    // (buffer loads: the compiler counts them exactly in its own waits,
+    // where global loads into LDS make it wait for everything)
+    const __amdgpu_buffer_rsrc_t wrs = rsrc_of(W_up), lrs = rsrc_of(lo_tiled);
+    auto issue = [&](const Item& it, int ks, int slot) {
+        uint4* sb = lds + slot * kUp2Stage;
+        const uint32_t wso = 2u * ((uint32_t)it.c0 * kRank + kKs * ks);
+        const uint32_t lso = 16u * ((uint32_t)(it.t0 / kTok) * kUpSteps * kLoTile + ks * kLoTile);
+        bdma16(wrs, sb + 64 * wave, 2u * wu_off[0], wso);
+        bdma16(wrs, sb + 64 * (wave + 8), 2u * wu_off[1], wso);
+        bdma16(lrs, sb + kUp2WChunks + 64 * wave, 16u * lo_off, lso);
+        bdma16(lrs, sb + kUp2WChunks + kLoTile + 64 * wave, 16u * lo_off, lso + 16u * kUpSteps * kLoTile);
+    };
+
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t aoff = 16 * panel_slot(n, g);
+    const int lrow = 16 * wl + n;
+    const uint32_t lo_a = 16 * (kUp2WChunks + kLoTile * hf + 8 * lrow + ((2 * g) ^ swz8(lrow)));
+    const uint32_t lo_b = 16 * (kUp2WChunks + kLoTile * hf + 8 * lrow + ((2 * g + 1) ^ swz8(lrow)));
+    auto read_first = [&](int slot, u32x4 (&lv)[2], u32x4 (&w0)[4]) {
+        const uint32_t sb = lds0 + 16 * slot * kUp2Stage;
+        lv[0] = ds_read16(sb + lo_a);
+        lv[1] = ds_read16(sb + lo_b);
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w0[k] = ds_read16_off<1024 * k>(sb + aoff); });
+    };
+    f32x4_t acc[4][4];  // [column block][stream]
+    // the other 12 W_up blocks are read one stream group ahead of their MFMAs
+    auto compute = [&](int slot, u32x4 (&lv)[2], u32x4 (&w0)[4]) {
+        const uint32_t wb = lds0 + 16 * slot * kUp2Stage + aoff;
+        u32x4 w1[4], w2[4], w3[4];
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w1[k] = ds_read16_off<1024 * (4 + k)>(wb); });
+        lgkm_wait<4>(lv[0], lv[1], w0[0], w0[1], w0[2], w0[3]);
+        uint32_t hi[8], mi[8] = {}, l3[8] = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (BF16_LO)  // the fast mode: lo rounded to bf16 (nearest even), one piece
+                hi[e] = __builtin_bit_cast(uint16_t, (__bf16)__uint_as_float(lv[e >> 2][e & 3]));
+            else
+                split3(__uint_as_float(lv[e >> 2][e & 3]), hi[e], mi[e], l3[e]);
+        }
+        u32x4 y[3];
+        y[0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        y[1] = u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)};
+        y[2] = u32x4{l3[0] | (l3[1] << 16), l3[2] | (l3[3] << 16), l3[4] | (l3[5] << 16), l3[6] | (l3[7] << 16)};
+        auto group = [&](int s, u32x4 (&w)[4]) {
+#pragma unroll
+            for (int p = BF16_LO ? 0 : 2; p >= 0; --p)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[cb][s] = mfma16(w[cb], y[p], acc[cb][s]);
+        };
+        group(0, w0);
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w2[k] = ds_read16_off<1024 * (8 + k)>(wb); });
+        lgkm_wait<4>(w1[0], w1[1], w1[2], w1[3]);
+        group(1, w1);
+        static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; w3[k] = ds_read16_off<1024 * (12 + k)>(wb); });
+        lgkm_wait<4>(w2[0], w2[1], w2[2], w2[3]);
+        group(2, w2);
+        lgkm_wait<0>(w3[0], w3[1], w3[2], w3[3]);
+        group(3, w3);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Issue order per item: step ks loads stage ks + 4 of the item (ks < 6)
+    // or stage ks - 6 of the next (ks >= 6), then two R loads (ks < 8); the
+    // item ends with its 12 store instructions (full pairs: every row
+    // stores).  The wait closing step ks needs stage ks + 2 landed and leaves
+    // in flight what was issued after it: 22, 24 (the previous item's stores
+    // included), 14 .. 14, 12, and after the item's stores, 22.  Before the
+    // first item 12 stores that write nothing (offsets past a 0-byte buffer
+    // resource) stand in for a previous item's, so every item waits alike.
+    constexpr int kStores = 12;
+    u32x4 lv[2], w0[4];
+    const int grid = gridDim.x;
+    int w = blockIdx.x;
+    Item cur = item_of(w);
+    Item nxt = w + grid < items ? item_of(w + grid) : cur;
+    static_for<0, 4>([&](auto kc) { constexpr int k = decltype(kc)::value; issue(cur, k, k); });
+    order();
+    {
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(out_mixed, 0, 0, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < kStores; ++k) {
+            __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4u * lane, 256u * k, 0);
+            order();
+        }
+    }
+    order();
+    ring_barrier<2 * kUp2Loads + kStores>();  // stages 0 and 1 landed everywhere
+    read_first(0, lv, w0);
+    while (true) {
+        const int t = cur.t0 + kTok * hf + lrow;  // every token of a full pair is < T
+        const uint32_t roff = 4u * ((uint32_t)t * kD + cur.c0 + 4 * g);  // (bytes; R of a chunk is < 2 GB)
+        float4 rv[4][4];  // [column block][stream]
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc[cb][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        static_for<0, kUpSteps>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            if constexpr (ks + 4 < kUpSteps)
+                issue(cur, ks + 4, (ks + 4) % kUp2Slots);
+            else
+                issue(nxt, ks - 6, (ks + 4) % kUp2Slots);
+            order();
+            if constexpr (ks < 8) {
+#pragma unroll
+                for (int j = 2 * ks; j < 2 * ks + 2; ++j) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rrs, roff, 4u * ((j & 3) * kWidth + 16 * (j >> 2)), 0);
+                    rv[j >> 2][j & 3] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                                                    __uint_as_float(v[3]));
+                }
+            }
+            order();
+            compute(ks % kUp2Slots, lv, w0);
+            if constexpr (ks + 1 < kUpSteps) {
+                read_first((ks + 1) % kUp2Slots, lv, w0);
+                ring_barrier_lg<(ks < 2 ? 10 + 2 * ks + kStores : ks == 8 ? 12 : 14), 6>();
+            }
+        });
+        // every wave is done with ring slot 4 (stage 9) before it takes the mixed values
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const uint32_t tb = lds0 + 16 * 4 * kUp2Stage + 4096 * wave;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
+                                   {rv[cb][1].x, rv[cb][1].y, rv[cb][1].z, rv[cb][1].w},
+                                   {rv[cb][2].x, rv[cb][2].y, rv[cb][2].z, rv[cb][2].w},
+                                   {rv[cb][3].x, rv[cb][3].y, rv[cb][3].z, rv[cb][3].w}};
+            float m[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                m[e] = (acc[cb][0][e] * r[0][e] + acc[cb][1][e] * r[1][e]) +
+                       (acc[cb][2][e] * r[2][e] + acc[cb][3][e] * r[3][e]);
+            ds_write16(tb + 256 * n + 16 * ((4 * cb + g) ^ n),
+                       u32x4{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])});
+        }
+        u32x4 mv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = (lane >> 4) + 4 * k, ch = lane & 15;
+            mv[k] = ds_read16(tb + 256 * row + 16 * (ch ^ row));
+        }
+        lds_wait(mv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = (lane >> 4) + 4 * k, ch = lane & 15;
+            const int tt = cur.t0 + kTok * hf + 16 * wl + row;
+            const size_t o = (size_t)tt * kWidth + cur.c0 + 4 * ch;
+            const float m[4] = {__uint_as_float(mv[k][0]), __uint_as_float(mv[k][1]), __uint_as_float(mv[k][2]),
+                                __uint_as_float(mv[k][3])};
+            *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
+            uint32_t bh[4], hh[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bh[e] = __builtin_bit_cast(uint16_t, (__bf16)m[e]);
+                hh[e] = __builtin_bit_cast(uint16_t, (_Float16)m[e]);
+            }
+            *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
+            *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        }
+        w += grid;
+        if (w >= items)
+            break;
+        cur = nxt;
+        nxt = w + grid < items ? item_of(w + grid) : cur;
+        read_first(0, lv, w0);
+        ring_barrier_lg<10 + kStores, 6>();  // the next item's stage 1 landed; slot 4 free again
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the last item's extra stage loads land before exit)
 }
 
 int tiles_of(int tokens)
@@ -897,13 +1366,36 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
             return e;
         float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
         const bool narrow = tiles <= 4;  // 16-column tiles (measured: better up to 256 tokens)
-        const int grid3 = (narrow ? 4 : 1) * 8 * kGroupsPerXcd * tiles;
-        auto* up = narrow ? (Pc ? (bf16_lo ? prefill_upmix<true, true, 1> : prefill_upmix<true, false, 1>)
-                                : (bf16_lo ? prefill_upmix<false, true, 1> : prefill_upmix<false, false, 1>))
-                          : (Pc ? (bf16_lo ? prefill_upmix<true, true, 4> : prefill_upmix<true, false, 4>)
-                                : (bf16_lo ? prefill_upmix<false, true, 4> : prefill_upmix<false, false, 4>));
-        hipLaunchKernelGGL(up, dim3(grid3), dim3(256), 0, stream, Tc, planes, W_up, Rc, Pc, out_mixed + out_off,
-                           out_bf16 + out_off, out_fp16 + out_off, Cc);
+        if (narrow) {
+            auto* up = Pc ? (bf16_lo ? prefill_upmix<true, true> : prefill_upmix<true, false>)
+                          : (bf16_lo ? prefill_upmix<false, true> : prefill_upmix<false, false>);
+            hipLaunchKernelGGL(up, dim3(4 * 8 * kGroupsPerXcd * tiles), dim3(256), 0, stream, Tc, planes, W_up, Rc,
+                               Pc, out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
+        } else if (Pc) {
+            auto* up = bf16_lo ? prefill_upmix2<true, true> : prefill_upmix2<true, false>;
+            hipLaunchKernelGGL(up, dim3(8 * kGroupsPerXcd * ((tiles + 1) / 2)), dim3(kUp2Waves * 64), 0, stream, Tc,
+                               tiles, planes, W_up, Rc, Pc, out_mixed + out_off, out_bf16 + out_off,
+                               out_fp16 + out_off, Cc);
+        } else {
+            // full token pairs on the persistent kernel, a ragged last pair on its own
+            const int pairs = Tc / (2 * kTok), items = 8 * kGroupsPerXcd * pairs;
+            if (items > 0) {
+                auto* up = bf16_lo ? prefill_upmix3<true> : prefill_upmix3<false>;
+                hipLaunchKernelGGL(up, dim3(items < kPersistGrid ? items : kPersistGrid), dim3(kUp2Waves * 64), 0,
+                                   stream, Tc, items, planes, W_up, Rc, out_mixed + out_off, out_bf16 + out_off,
+                                   out_fp16 + out_off);
+            }
+            const int t_done = pairs * 2 * kTok;
+            if (t_done < Tc) {
+                const int rest = Tc - t_done;
+                auto* up = bf16_lo ? prefill_upmix2<false, true> : prefill_upmix2<false, false>;
+                hipLaunchKernelGGL(up, dim3(8 * kGroupsPerXcd), dim3(kUp2Waves * 64), 0, stream, rest,
+                                   tiles_of(rest), planes + (size_t)(t_done / kTok) * kUpSteps * kLoTile, W_up,
+                                   Rc + (size_t)t_done * kD, nullptr, out_mixed + out_off + (size_t)t_done * kWidth,
+                                   out_bf16 + out_off + (size_t)t_done * kWidth,
+                                   out_fp16 + out_off + (size_t)t_done * kWidth, nullptr);
+            }
+        }
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
