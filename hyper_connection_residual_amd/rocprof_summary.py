@@ -64,18 +64,40 @@ def stats(path: str) -> str:
     return "\n".join(out)
 
 
+def _clusters(d):
+    """Sorted durations split where one is more than 1.6x the one before (a
+    persistent kernel launched at several read sizes keeps its grid)."""
+    d = sorted(d)
+    out, cur = [], [d[0]]
+    for v in d[1:]:
+        if v > 1.6 * cur[-1] and len(cur) >= 3:
+            out.append(cur)
+            cur = []
+        cur.append(v)
+    out.append(cur)
+    return out
+
+
 def trace(path: str) -> str:
+    """The library's kernels (hc::) per (kernel, workgroup count); a group
+    whose durations fall into clusters more than 1.6x apart gets a row each."""
     groups = collections.defaultdict(list)
     with open(path) as f:
         for row in csv.DictReader(f):
+            if not row["Kernel_Name"].replace("void ", "").startswith("hc::"):
+                continue
             wgs = int(row["Grid_Size_X"]) // max(1, int(row["Workgroup_Size_X"]))
             dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
             groups[(short_name(row["Kernel_Name"]), wgs)].append(dur)
+    rows = []
+    for (name, wgs), d in groups.items():
+        cl = _clusters(d)
+        for i, c in enumerate(cl):
+            tag = "" if len(cl) == 1 else " (size %d of %d)" % (i + 1, len(cl))
+            rows.append((sum(c), "| %s%s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
+                name, tag, wgs, len(c), sum(c) / len(c), c[len(c) // 2], c[0], c[-1])))
     out = ["| kernel | workgroups | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
-    for (name, wgs), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        d = sorted(d)
-        out.append("| %s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
-            name, wgs, len(d), sum(d) / len(d), d[len(d) // 2], d[0], d[-1]))
+    out += [r for _, r in sorted(rows, key=lambda x: -x[0])]
     return "\n".join(out)
 
 
@@ -95,14 +117,35 @@ def read_traffic(md_path: str):
     return (val, h) if val is not None else None
 
 
-def _counter_rows(paths):
-    """{(kernel, workgroups): {counter: [value per dispatch]}} over counter runs."""
+def _counter_rows(paths, split=r"prefill_upmix3"):
+    """{(kernel, workgroups, size): {counter: [value per dispatch]}} over
+    counter runs.  A persistent kernel (`split`) keeps its grid at every read
+    size, so its dispatches are split by size: within each run they are
+    clustered by their summed counter values (clusters more than 1.6x apart),
+    and size i is the i-th smallest cluster of every run.  Other kernels keep
+    one row per grid (a grid run at several sizes is averaged over them)."""
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for path in paths:
+        disp = collections.defaultdict(dict)  # (kernel, wgs, dispatch id) -> {counter: value}
         with open(path) as f:
             for row in csv.DictReader(f):
                 wgs = int(row["Grid_Size"]) // max(1, int(row["Workgroup_Size"]))
-                acc[(short_name(row["Kernel_Name"]), wgs)][row["Counter_Name"]].append(float(row["Counter_Value"]))
+                disp[(short_name(row["Kernel_Name"]), wgs, row["Dispatch_Id"])][row["Counter_Name"]] = \
+                    float(row["Counter_Value"])
+        by_kernel = collections.defaultdict(list)
+        for (k, wgs, _), cs in disp.items():
+            by_kernel[(k, wgs)].append(cs)
+        for (k, wgs), ds in by_kernel.items():
+            ds.sort(key=lambda cs: sum(cs.values()))
+            size = 0
+            prev = None
+            for cs in ds:
+                tot = sum(cs.values())
+                if re.search(split, k) and prev is not None and prev > 0 and tot > 1.6 * prev:
+                    size += 1
+                prev = tot
+                for c, v in cs.items():
+                    acc[(k, wgs, size)][c].append(v)
     return acc
 
 
@@ -126,7 +169,8 @@ def counters(log_paths, csv_paths, kernels=r"hc::|copyBuffer") -> str:
     out = ["counters taken on kernel source hash %s" % run_hash, "",
            "| kernel | workgroups | dispatches | " + " | ".join(names) + " | derived |",
            "|---|---|---|" + "---|" * len(names) + "---|"]
-    for (k, wgs), cs in sorted(acc.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+    sizes = collections.Counter((k, wgs) for (k, wgs, _) in acc)
+    for (k, wgs, size), cs in sorted(acc.items()):
         if not re.search(kernels, k):
             continue
         mean = {c: sum(v) / len(v) for c, v in cs.items()}
@@ -147,7 +191,8 @@ def counters(log_paths, csv_paths, kernels=r"hc::|copyBuffer") -> str:
             der.append("MFMA busy %.1f %%" % (100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (32 * mean["SQ_BUSY_CYCLES"])))
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
             der.append("bf16 MFMA %.2f GFLOP" % (512 * mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / 1e9))
-        out.append("| %s | %d | %d | " % (k, wgs, n) + " | ".join(
+        tag = "" if sizes[(k, wgs)] == 1 else " (size %d of %d)" % (size + 1, sizes[(k, wgs)])
+        out.append("| %s%s | %d | %d | " % (k, tag, wgs, n) + " | ".join(
             ("%.4g" % mean[c]) if c in mean else "" for c in names) + " | " + "; ".join(der) + " |")
     if sweep:
         out += ["", "short-window kernel HBM bytes per launch (sweep average): %d" % round(sum(sweep) / len(sweep)),
