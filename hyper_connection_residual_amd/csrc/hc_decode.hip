@@ -37,8 +37,10 @@
 //   with tokens as the M dimension.  Each fp32 activation is split exactly into
 //   three bf16 pieces (hi + mid + lo3 == x), so every product is exact and the
 //   result stays fp32-faithful.  The pieces of all tokens share the MFMA's
-//   rows (row p T + t: piece p of token t), so one chain of MFMAs carries them
-//   when 3 T <= 16, and 2, 3 or 6 chains for more tokens.
+//   rows.  Up to 8 tokens row 4 t + p holds piece p of token t (one chain of
+//   MFMAs per 4 tokens): a token's three products then sit in one lane, which
+//   sums them and mixes the streams in registers.  Above 8 tokens row p T + t
+//   holds them (3 or 6 chains) and the products go through LDS.
 // * Two hand-offs, no grid barrier.  XCD x owns lo rows [40 x, 40 x + 40): 14
 //   of its 32 workgroups each reduce the 32 partials of 3 rows through the
 //   XCD's L2 (hop 1, one wave; two above 8 tokens) and publish lo device-wide; every workgroup gathers all of lo
@@ -151,6 +153,24 @@ __host__ __device__ constexpr int chain_rows(int c)
 {
     return kChains<T> == 6 ? ((c & 1) ? T - 16 : 16) : (c == 0 ? kPackRows<T> : T);
 }
+// Up to 8 tokens the blocks take the quad layout instead: A row 4 t + p holds
+// piece p of token t (row 4 t + 3 is never written and feeds a D row nobody
+// reads), one chain per 4 tokens.  The D layout then puts a token's three
+// pieces into one lane (row i of column n sits in lane n + 16 (i / 4), element
+// i % 4), so pieces are summed and the streams mixed in registers, with no
+// product block going through LDS.
+template <int T>
+constexpr bool kQuad = T <= 8;
+template <int T>
+constexpr int kQuadChains = (T + 3) / 4;
+// Rows of a y or lo plane set and the row of (piece p, token t) in it.
+template <int T>
+constexpr int kPlaneRows = kQuad<T> ? 16 * kQuadChains<T> : 3 * T;
+template <int T>
+__host__ __device__ constexpr int plane_row(int p, int t)
+{
+    return kQuad<T> ? 4 * t + p : p * T + t;
+}
 // Chains' room in the LDS product blocks (at least 2, as laid out for 1..8 tokens).
 template <int T>
 constexpr int kCombChains = kChains<T> < 2 ? 2 : kChains<T>;
@@ -159,21 +179,22 @@ constexpr int kCombChains = kChains<T> < 2 ? 2 : kChains<T>;
 template <int T>
 constexpr int kTokSlots = T <= 8 ? 8 : (T <= 16 ? 16 : 32);
 
-// LDS map (bytes): both weight tiles, the y planes [3 T][kYRow] bf16, the
-// token sums of squares of the items [T][80] fp32, the down product blocks
-// [6][chains][64] f32x4, the lo planes [3 T][kLoRow] bf16, R' of the up
-// tile's rows [T][40] fp32, the up product blocks [3][chains][64] f32x4.
+// LDS map (bytes): both weight tiles, the y planes [kPlaneRows][kYRow] bf16,
+// the token sums of squares of the items [T][80] fp32, the down product blocks
+// [6][chains][64] f32x4, the lo planes [kPlaneRows][kLoRow] bf16, R' of the up
+// tile's rows [T][40] fp32, the up product blocks [3][chains][64] f32x4 (up to
+// 8 tokens the product blocks and R' are laid out but unused).
 // Above 16 tokens, regions never live at once share memory (kShare): the W_up
 // tile lands where the W_down tile was (it is issued after the down MFMAs),
 // the lo planes overwrite the y planes, the up product blocks the down ones.
 template <int T> constexpr bool kShare = T > 16;
 template <int T> constexpr size_t kOffUTile = kShare<T> ? 0 : 16 * kTileChunks;
 template <int T> constexpr size_t kOffY = kOffUTile<T> + 16 * kTileChunks;
-template <int T> constexpr size_t kOffSs = kOffY<T> + 2 * 3 * T * kYRow;
+template <int T> constexpr size_t kOffSs = kOffY<T> + 2 * kPlaneRows<T> * kYRow;
 template <int T> constexpr size_t kOffComb = kOffSs<T> + 4 * T * kStageItems;
 template <int T> constexpr size_t kOffLo = kShare<T> ? kOffY<T> : kOffComb<T> + 6 * kCombChains<T> * 64 * 16;
 template <int T>
-constexpr size_t kOffRp = kShare<T> ? kOffComb<T> + 6 * kCombChains<T> * 64 * 16 : kOffLo<T> + 2 * 3 * T * kLoRow;
+constexpr size_t kOffRp = kShare<T> ? kOffComb<T> + 6 * kCombChains<T> * 64 * 16 : kOffLo<T> + 2 * kPlaneRows<T> * kLoRow;
 template <int T> constexpr size_t kOffUComb = kShare<T> ? kOffComb<T> : kOffRp<T> + 4 * T * kUpRows;
 template <int T>
 constexpr size_t kLdsBytes = kShare<T> ? kOffRp<T> + 4 * T * kUpRows : kOffUComb<T> + 3 * kCombChains<T> * 64 * 16;
@@ -485,23 +506,40 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     }
     // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
-    //     and R and pending of those 40 (stream, column) pairs, for the mix
-    constexpr int kUpPasses = (kUpRows * T + kDecThreads - 1) / kDecThreads;  // 1, 2 above 12 tokens, 3 above 25
+    //     and R and pending of those 40 (stream, column) pairs, for the mix.
+    //     Above 8 tokens thread j's pass pp holds item j + 512 pp = 40 t + row
+    //     (staged through LDS); in the quad layout lane (n, g) of wave w < 3
+    //     holds, in slot c, token 4 c + g of the tile row its up products
+    //     land on (tokens past T re-read token 0).
+    constexpr int kUpPasses = kQuad<T> ? kQuadChains<T> : (kUpRows * T + kDecThreads - 1) / kDecThreads;
     float mr[kUpPasses], mp[kUpPasses];
+    const int up_row = wave < 2 ? 16 * wave + n : 32 + (n & 7);  // (quad layout, waves 0..2)
     auto issue_up = [&]() {
         for (int q = wave; q < kTileInstr; q += 8) {
             int row, j;
             tile_lane<kRowChunks>(q, lane, row, j);
             dma16(W_up + (size_t)((row & 3) * kWidth + c0 + (row >> 2)) * kRank + 8 * j, utile + 64 * q);
         }
+        if constexpr (kQuad<T>) {
+            if (wave < 3) {
 #pragma unroll
-        for (int pp = 0; pp < kUpPasses; ++pp) {
-            const int it = threadIdx.x + kDecThreads * pp;
-            const int itc = it < kUpRows * T ? it : 0;
-            const int at = itc / kUpRows, row = itc - at * kUpRows;
-            const size_t o = (size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2);
-            mr[pp] = R[o];
-            mp[pp] = Pm[o];
+                for (int c = 0; c < kUpPasses; ++c) {
+                    const int t = 4 * c + g;
+                    const size_t o = (size_t)(t < T ? t : 0) * kD + (up_row & 3) * kWidth + c0 + (up_row >> 2);
+                    mr[c] = R[o];
+                    mp[c] = Pm[o];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int pp = 0; pp < kUpPasses; ++pp) {
+                const int it = threadIdx.x + kDecThreads * pp;
+                const int itc = it < kUpRows * T ? it : 0;
+                const int at = itc / kUpRows, row = itc - at * kUpRows;
+                const size_t o = (size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2);
+                mr[pp] = R[o];
+                mp[pp] = Pm[o];
+            }
         }
     };
 
@@ -525,9 +563,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
             sspart[at * kStageItems + f] = ss;
             const int col = 4 * f;
-            *reinterpret_cast<uint2*>(&ypl[(0 * T + at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-            *reinterpret_cast<uint2*>(&ypl[(1 * T + at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-            *reinterpret_cast<uint2*>(&ypl[(2 * T + at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(0, at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(1, at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
+            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(2, at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
         }
     }
     wait_all_loads();  // this wave's part of the W_down tile is in LDS
@@ -537,44 +575,83 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     pin(seen);
     const uint32_t gen = ((uint32_t)__builtin_amdgcn_readfirstlane((int)seen) + 1u) & kGenMask;
 
-    // (7) down projection: wave w < 6 takes rows 16 (w % 3) .. +15 of the
-    //     tile (block 2: rows 32..39, its upper 8 slots repeat them) over K
-    //     steps 5 (w / 3) .. +4 of 32 columns.  A rows are (piece, token)
-    //     pairs in the planes' own order (row p T + t: piece p of token t), so
-    //     one chain of MFMAs carries all three pieces when 3 T <= 16, and 2, 3
-    //     or 6 chains carry them for more tokens (kChains).
-    if (wave < 6) {
-        constexpr int NC = kChains<T>;
-        const int nb = wave % 3, kh = wave / 3;
-        const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
-        // all operands first (one LDS latency, not five); A rows past the
-        // pieces re-read the chain's first row: they only feed D rows nobody reads
-        int ar[NC];
+    // (7) down projection.  Above 8 tokens wave w < 6 takes rows 16 (w % 3)
+    //     .. +15 of the tile (block 2: rows 32..39, its upper 8 slots repeat
+    //     them) over K steps 5 (w / 3) .. +4 of 32 columns.  A rows are
+    //     (piece, token) pairs in the planes' own order (row p T + t: piece p
+    //     of token t), so 2, 3 or 6 chains carry the pieces (kChains).  Up to
+    //     8 tokens (quad layout) wave w < 3 takes rows 16 w .. +15 over all 10
+    //     K steps, and lane (n, g) of chain c ends with the three pieces'
+    //     products of token 4 c + g, row 16 w + n, in elements 0..2.
+    if (wave < (kQuad<T> ? 3 : 6)) {
+        if constexpr (kQuad<T>) {
+            // (7q, 8q) products, then the partial dots straight into the
+            //     XCD's L2: hi + (mid + lo3) per token, all 8 token slots
+            //     (whole lines; slots >= T hold 0)
+            constexpr int NC = kQuadChains<T>;
+            const int row = wave < 2 ? 16 * wave + n : 32 + (n & 7);
+            uint4 wb[10], a[NC][10];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            ar[c] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
-        uint4 wb[5], a[NC][5];
+            for (int q = 0; q < 10; ++q) {
+                const int col = 32 * q + 8 * g;
+                wb[q] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
 #pragma unroll
-        for (int qq = 0; qq < 5; ++qq) {
-            const int q = 5 * kh + qq;
-            const int col = 32 * q + 8 * g;
-            wb[qq] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
+                for (int c = 0; c < NC; ++c)
+                    a[c][q] = *reinterpret_cast<const uint4*>(&ypl[(16 * c + m) * kYRow + col]);
+            }
+            f32x4_t acc[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                a[c][qq] = *reinterpret_cast<const uint4*>(&ypl[ar[c] * kYRow + col]);
+                acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 10; ++q)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[c] = mfma16(a[c][q], wb[q], acc[c]);
+            HC_PROBE(2, threadIdx.x == 0);
+            if (wave < 2 || n < 8) {  // (block 2's upper slots are copies)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int t = 4 * h + g;
+                    const f32x4_t d = acc[h < NC ? h : 0];
+                    const float v = h < NC && t < T ? d[0] + (d[1] + d[2]) : 0.f;
+                    st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kTokSlots<T> + t,
+                                tag_f32(v, xcd_tag(gen, rot)));
+                }
+            }
+        } else {
+            constexpr int NC = kChains<T>;
+            const int nb = wave % 3, kh = wave / 3;
+            const int row = nb < 2 ? 16 * nb + n : 32 + (n & 7);
+            // all operands first (one LDS latency, not five); A rows past the
+            // pieces re-read the chain's first row: they only feed D rows nobody reads
+            int ar[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                ar[c] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
+            uint4 wb[5], a[NC][5];
+#pragma unroll
+            for (int qq = 0; qq < 5; ++qq) {
+                const int q = 5 * kh + qq;
+                const int col = 32 * q + 8 * g;
+                wb[qq] = dtile[tile_pos<kRowChunks>(row, 4 * q + g)];
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    a[c][qq] = *reinterpret_cast<const uint4*>(&ypl[ar[c] * kYRow + col]);
+            }
+            f32x4_t acc[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qq = 0; qq < 5; ++qq)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[c] = mfma16(a[c][qq], wb[qq], acc[c]);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                comb[(wave * NC + c) * 64 + lane] = acc[c];
         }
-        f32x4_t acc[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int qq = 0; qq < 5; ++qq)
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                acc[c] = mfma16(a[c][qq], wb[qq], acc[c]);
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            comb[(wave * NC + c) * 64 + lane] = acc[c];
     } else if (wave == 6 || (T > 16 && wave == 7)) {
         // (7') meanwhile, the slice's sum of squares per token: lane 8 t + p
         //      sums 10 of token t's 80 item sums, then the 8 lanes combine theirs
@@ -607,25 +684,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 st_word_xcd(&s.ssq[((size_t)x * kDecWgPerXcd + i) * kSsqLine<T> + tt], tag_f32(ss, xcd_tag(gen, rot)));
         }
     }
-    HC_PROBE(2, threadIdx.x == 0);
-    wg_barrier();  // Bc1: every product block in LDS
+    if constexpr (!kQuad<T>) {
+        HC_PROBE(2, threadIdx.x == 0);
+        wg_barrier();  // Bc1: every product block in LDS
 
-    if (wave < 6) {
-        // (8) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g, into
-        //     the XCD's L2: per K half hi + (mid + lo3), then the two halves
-        //     (all 8 token slots, whole lines; slots >= T hold 0)
-        //     (above 8 tokens each lane also takes tokens t + 8, t + 16, ...:
-        //     16 or 32 slots)
-        const float* cf = reinterpret_cast<const float*>(comb);
-        const int nb = wave % 3, t = 4 * (wave / 3) + g;
-        const int row = 16 * nb + n;
-        if (row < kDecRowsPerXcd) {
+        if (wave < 6) {
+            // (8) partial dots of rows 16 (w % 3) + n, token 4 (w / 3) + g, into
+            //     the XCD's L2: per K half hi + (mid + lo3), then the two halves
+            //     (all 8 token slots, whole lines; slots >= T hold 0)
+            //     (above 8 tokens each lane also takes tokens t + 8, t + 16, ...:
+            //     16 or 32 slots)
+            const float* cf = reinterpret_cast<const float*>(comb);
+            const int nb = wave % 3, t = 4 * (wave / 3) + g;
+            const int row = 16 * nb + n;
+            if (row < kDecRowsPerXcd) {
 #pragma unroll
-            for (int h = 0; h < kTokSlots<T> / 8; ++h) {
-                const int th = t + 8 * h;
-                const float v = th < T ? piece_sum<T>(cf, nb, th, n) + piece_sum<T>(cf, nb + 3, th, n) : 0.f;
-                st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kTokSlots<T> + th,
-                            tag_f32(v, xcd_tag(gen, rot)));
+                for (int h = 0; h < kTokSlots<T> / 8; ++h) {
+                    const int th = t + 8 * h;
+                    const float v = th < T ? piece_sum<T>(cf, nb, th, n) + piece_sum<T>(cf, nb + 3, th, n) : 0.f;
+                    st_word_xcd(s.part + (((size_t)x * kDecWgPerXcd + i) * kDecRowsPerXcd + row) * kTokSlots<T> + th,
+                                tag_f32(v, xcd_tag(gen, rot)));
+                }
             }
         }
     }
@@ -885,9 +964,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                         const int jr = kDecRowsPerXcd * wave + rowl;
                         uint32_t hb, mb, lb;
                         split3(__uint_as_float(h ? lw[k].z : lw[k].x), hb, mb, lb);
-                        lpl[(0 * T + tt) * kLoRow + jr] = (uint16_t)hb;
-                        lpl[(1 * T + tt) * kLoRow + jr] = (uint16_t)mb;
-                        lpl[(2 * T + tt) * kLoRow + jr] = (uint16_t)lb;
+                        lpl[plane_row<T>(0, tt) * kLoRow + jr] = (uint16_t)hb;
+                        lpl[plane_row<T>(1, tt) * kLoRow + jr] = (uint16_t)mb;
+                        lpl[plane_row<T>(2, tt) * kLoRow + jr] = (uint16_t)lb;
                     }
                 }
             }
@@ -900,7 +979,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     for (int pp = 0; pp < kUpPasses; ++pp) {
         rprime[pp] = P ? mr[pp] + mp[pp] : mr[pp];
         const int it = threadIdx.x + kDecThreads * pp;  // it = 40 t + row
-        if (it < kUpRows * T)
+        if (!kQuad<T> && it < kUpRows * T)
             rpl[it] = rprime[pp];
     }
     wg_barrier();  // B2: lo and R' staged, W_up tile complete
@@ -912,76 +991,132 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //      stored the partials that hop 2 has just waited for, and no other
     //      workgroup mixes these columns.  (After an expired wait that is not
     //      known: nothing is committed.)
+    if constexpr (kQuad<T>) {
+        // (each (stream, column, token) once: block 2's upper slots are copies)
+        if (R_commit && P && !poisoned && wave < 3 && (wave < 2 || n < 8)) {
 #pragma unroll
-    for (int pp = 0; pp < kUpPasses; ++pp) {
-        const int it = threadIdx.x + kDecThreads * pp;
-        if (R_commit && P && !poisoned && it < kUpRows * T) {
-            const int at = it / kUpRows, row = it - at * kUpRows;
-            R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime[pp];
+            for (int c = 0; c < kUpPasses; ++c)
+                if (4 * c + g < T)
+                    R_commit[(size_t)(4 * c + g) * kD + (up_row & 3) * kWidth + c0 + (up_row >> 2)] = rprime[c];
+        }
+    } else {
+#pragma unroll
+        for (int pp = 0; pp < kUpPasses; ++pp) {
+            const int it = threadIdx.x + kDecThreads * pp;
+            if (R_commit && P && !poisoned && it < kUpRows * T) {
+                const int at = it / kUpRows, row = it - at * kUpRows;
+                R_commit[(size_t)at * kD + (row & 3) * kWidth + c0 + (row >> 2)] = rprime[pp];
+            }
         }
     }
 
-    constexpr bool kSplitUp = kChains<T> == 6;  // above 16 tokens: one token half per wave
-    if (wave < (kSplitUp ? 6 : 3)) {
-        // (11) up projection: wave w takes tile rows 16 rb .. +15, rb = w % 3
-        //      (slot n = 4 column + stream; block 2: rows 32..39, its upper 8
-        //      slots repeat them), all 10 K steps, A rows packed as in the down
-        //      projection (above 16 tokens: waves 0-2 the chains of tokens
-        //      0..15, waves 3-5 those of tokens 16..); gated = up (identity
-        //      epilogue); then the mix of the 4 streams of a column
-        constexpr int UC = kSplitUp ? 3 : kChains<T>;  // chains per wave
-        const int rb = wave % 3, th = kSplitUp ? wave / 3 : 0;
-        const int row = rb < 2 ? 16 * rb + n : 32 + (n & 7);
-        const int st = n & 3;
-        int ar[UC];
+    if constexpr (kQuad<T>) {
+        if (wave < 3) {
+            // (11q) up projection, quad layout: wave w takes tile rows 16 w ..
+            //      +15 (slot n = 4 column + stream; block 2: rows 32..39, its
+            //      upper 8 slots repeat them), all 10 K steps; lane (n, g) of
+            //      chain c ends with the pieces of token 4 c + g in elements
+            //      0..2: up = hi + (mid + lo3); gated = up (identity
+            //      epilogue); then the mix of the 4 streams of a column
+            //      ((s0 + s1) + (s2 + s3), across the lane quad)
+            constexpr int NC = kQuadChains<T>;
+            uint4 wb[10], a[NC][10];
 #pragma unroll
-        for (int j = 0; j < UC; ++j) {
-            const int c = kSplitUp ? 2 * j + th : j;
-            ar[j] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
-        }
-        uint4 wb[10], a[UC][10];
+            for (int q = 0; q < 10; ++q) {
+                const int jc = 32 * q + 8 * g;
+                wb[q] = utile[tile_pos<kRowChunks>(up_row, 4 * q + g)];
 #pragma unroll
-        for (int q = 0; q < 10; ++q) {
-            const int jc = 32 * q + 8 * g;
-            wb[q] = utile[tile_pos<kRowChunks>(row, 4 * q + g)];
-#pragma unroll
-            for (int j = 0; j < UC; ++j)
-                a[j][q] = *reinterpret_cast<const uint4*>(&lpl[ar[j] * kLoRow + jc]);
-        }
-        f32x4_t acc[UC];
-#pragma unroll
-        for (int j = 0; j < UC; ++j)
-            acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 10; ++q)
-#pragma unroll
-            for (int j = 0; j < UC; ++j)
-                acc[j] = mfma16(a[j][q], wb[q], acc[j]);
-        // a token's pieces sit in other lanes: through this wave's own LDS block
-        f32x4_t* const ub = ucomb + wave * UC * 64;
-#pragma unroll
-        for (int j = 0; j < UC; ++j)
-            ub[64 * j + lane] = acc[j];
-        asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
-        const float* cf = reinterpret_cast<const float*>(ub);
-        const int c = c0 + (row >> 2);
-        const bool owner = st == 0 && (rb < 2 || n < 8);  // (block 2's upper slots are copies)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i16 = 4 * g + e, tt = 16 * th + i16;
-            // block j holds piece j of tokens 16 th + i16 (row i16 of the block)
-            auto at = [&](int j) { return cf[(64 * j + n + 16 * (i16 >> 2)) * 4 + (i16 & 3)]; };
-            const float up = tt < T ? (kSplitUp ? at(0) + (at(1) + at(2)) : piece_sum<T>(cf, 0, tt, n)) : 0.f;
-            const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
-            const float mixed = poisoned ? __builtin_nanf("") : sum4(up * rp);  // (s0 + s1) + (s2 + s3)
-            if (owner && tt < T) {
-                const size_t o = (size_t)tt * kWidth + c;
-                out_mixed[o] = mixed;
-                out_bf16[o] = __builtin_bit_cast(uint16_t, (__bf16)mixed);
-                out_fp16[o] = __builtin_bit_cast(uint16_t, (_Float16)mixed);
+                for (int c = 0; c < NC; ++c)
+                    a[c][q] = *reinterpret_cast<const uint4*>(&lpl[(16 * c + m) * kLoRow + jc]);
             }
+            f32x4_t acc[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 10; ++q)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[c] = mfma16(a[c][q], wb[q], acc[c]);
+            const int col = c0 + (up_row >> 2);
+            const bool owner = (n & 3) == 0 && (wave < 2 || n < 8);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int t = 4 * c + g;
+                const float up = acc[c][0] + (acc[c][1] + acc[c][2]);
+                const float mixed = poisoned ? __builtin_nanf("") : sum4(up * rprime[c]);
+                if (owner && t < T) {
+                    const size_t o = (size_t)t * kWidth + col;
+                    out_mixed[o] = mixed;
+                    out_bf16[o] = __builtin_bit_cast(uint16_t, (__bf16)mixed);
+                    out_fp16[o] = __builtin_bit_cast(uint16_t, (_Float16)mixed);
+                }
+            }
+            HC_PROBE(9, wave == 0 && lane == 0);
         }
-        HC_PROBE(9, wave == 0 && lane == 0);
+    } else {
+        constexpr bool kSplitUp = kChains<T> == 6;  // above 16 tokens: one token half per wave
+        if (wave < (kSplitUp ? 6 : 3)) {
+            // (11) up projection: wave w takes tile rows 16 rb .. +15, rb = w % 3
+            //      (slot n = 4 column + stream; block 2: rows 32..39, its upper 8
+            //      slots repeat them), all 10 K steps, A rows packed as in the down
+            //      projection (above 16 tokens: waves 0-2 the chains of tokens
+            //      0..15, waves 3-5 those of tokens 16..); gated = up (identity
+            //      epilogue); then the mix of the 4 streams of a column
+            constexpr int UC = kSplitUp ? 3 : kChains<T>;  // chains per wave
+            const int rb = wave % 3, th = kSplitUp ? wave / 3 : 0;
+            const int row = rb < 2 ? 16 * rb + n : 32 + (n & 7);
+            const int st = n & 3;
+            int ar[UC];
+#pragma unroll
+            for (int j = 0; j < UC; ++j) {
+                const int c = kSplitUp ? 2 * j + th : j;
+                ar[j] = chain_base<T>(c) + (m < chain_rows<T>(c) ? m : 0);
+            }
+            uint4 wb[10], a[UC][10];
+#pragma unroll
+            for (int q = 0; q < 10; ++q) {
+                const int jc = 32 * q + 8 * g;
+                wb[q] = utile[tile_pos<kRowChunks>(row, 4 * q + g)];
+#pragma unroll
+                for (int j = 0; j < UC; ++j)
+                    a[j][q] = *reinterpret_cast<const uint4*>(&lpl[ar[j] * kLoRow + jc]);
+            }
+            f32x4_t acc[UC];
+#pragma unroll
+            for (int j = 0; j < UC; ++j)
+                acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 10; ++q)
+#pragma unroll
+                for (int j = 0; j < UC; ++j)
+                    acc[j] = mfma16(a[j][q], wb[q], acc[j]);
+            // a token's pieces sit in other lanes: through this wave's own LDS block
+            f32x4_t* const ub = ucomb + wave * UC * 64;
+#pragma unroll
+            for (int j = 0; j < UC; ++j)
+                ub[64 * j + lane] = acc[j];
+            asm volatile("" ::: "memory");  // (LDS operations of one wave complete in order)
+            const float* cf = reinterpret_cast<const float*>(ub);
+            const int c = c0 + (row >> 2);
+            const bool owner = st == 0 && (rb < 2 || n < 8);  // (block 2's upper slots are copies)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i16 = 4 * g + e, tt = 16 * th + i16;
+                // block j holds piece j of tokens 16 th + i16 (row i16 of the block)
+                auto at = [&](int j) { return cf[(64 * j + n + 16 * (i16 >> 2)) * 4 + (i16 & 3)]; };
+                const float up = tt < T ? (kSplitUp ? at(0) + (at(1) + at(2)) : piece_sum<T>(cf, 0, tt, n)) : 0.f;
+                const float rp = rpl[(tt < T ? tt : 0) * kUpRows + row];
+                const float mixed = poisoned ? __builtin_nanf("") : sum4(up * rp);  // (s0 + s1) + (s2 + s3)
+                if (owner && tt < T) {
+                    const size_t o = (size_t)tt * kWidth + c;
+                    out_mixed[o] = mixed;
+                    out_bf16[o] = __builtin_bit_cast(uint16_t, (__bf16)mixed);
+                    out_fp16[o] = __builtin_bit_cast(uint16_t, (_Float16)mixed);
+                }
+            }
+            HC_PROBE(9, wave == 0 && lane == 0);
+        }
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&s.gen[b], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
