@@ -7,6 +7,10 @@ of T = 1..8 tokens with a pending write, 48 independent weight sets (631 MB,
 more than the 256 MB Infinity Cache) rotated per read so every read streams its
 13,148,160 weight bytes from HBM.  One step = one sweep T = 1..8 (8 reads, each
 on the next weight set).  Inputs are resident in HBM before timing starts.
+Before the K timed steps run at least W untimed steps, and as many more as it
+takes to keep the GPU busy for 60 ms: the engine clock of an idle GPU ramps up
+over its first tens of milliseconds of work, and the timed steps measure the
+steady state of back-to-back reads (`warmup_run` says what ran).
 
 Prints ONE JSON line.  `value` = weight bytes streamed per second over the
 timed sweeps (GB/s), one hc_read call per read; the same sweeps replayed from
@@ -41,6 +45,7 @@ N_SETS = 48
 TS = list(range(1, 9))
 WINDOWS = [9, 12, 16, 17, 24, 32, 33, 48, 64, 128, 256, 512]  # reads above 8 tokens, timed beside the sweep
 WARM_WIDE_MS = 60.0  # GPU time of untimed wide reads before each prefill timing (engine clock ramp)
+WARM_STEP_MS = 60.0  # GPU time of untimed sweep steps (at least --warmup of them) before the timed steps
 
 
 def parse():
@@ -186,9 +191,20 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
+    def warm_steps(s, body):
+        # at least --warmup untimed steps, continued until WARM_STEP_MS of GPU
+        # time has passed: the engine clock of an idle GPU ramps up over the
+        # first tens of milliseconds of work, and the timed steps measure the
+        # steady state of back-to-back reads
+        done, ms = 0, 0.0
+        while done < args.warmup or ms < (5.0 if args.light else WARM_STEP_MS):
+            n = max(args.warmup - done, 20)
+            ms += time_region(s, lambda k: body(done + k), n)
+            done += n
+        return {"steps": done, "gpu_ms": round(ms, 1)}
+
     # ---- eager: one hc_read call per read, back to back on one stream
-    for k in range(args.warmup):
-        eager_step(k)
+    warm_eager = warm_steps(stream, eager_step)
     t0 = time.perf_counter()
     ms_eager = time_region(stream, eager_step, args.steps)
     print("# eager: %d steps, %.3f ms/step (event), wall %.3f s"
@@ -387,9 +403,7 @@ def main():
             for i, T in enumerate(TS):
                 read_on(T, (len(TS) * j + i) % N_SETS, gstream)
         step_graphs.append(g)
-    for k in range(args.warmup):
-        with torch.cuda.stream(gstream):
-            step_graphs[k % n_pos].replay()
+    warm_graph = warm_steps(gstream, lambda k: step_graphs[k % n_pos].replay())
     t0 = time.perf_counter()
     ms_graph = time_region(gstream, lambda k: step_graphs[k % n_pos].replay(), args.steps)
     print("# graph: %d steps, %.3f ms/step (event), wall %.3f s"
@@ -423,6 +437,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"eager": warm_eager, "graph": warm_graph},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -91,6 +91,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTileChunks = 1600;           // 16-byte chunks in either weight tile (25,600 bytes)
 constexpr int kTileInstr = kTileChunks / 64;  // wave instructions per tile (25)
@@ -102,8 +103,8 @@ constexpr int kLoRow = kRank + 8;           // padded LDS row of a lo plane (bf1
 // Scratch layout (in 64-bit words from the base): partial dots, slice sums of
 // squares, lo, then the 32-bit generation counters and the timeout counter.
 // Every producer writes whole 128-byte lines (16 words), padding unused token
-// slots: a line the XCD's L2 holds only in part is filled from memory when it
-// is read, which costs a memory round trip instead of an L2 hit.
+// slots: a line an L2 holds only in part is filled from memory before it is
+// read or written through, which costs a memory round trip.
 //   part [8 xcd][32 wg][40 rows][8 token slots]     (two rows per line), or
 //        [8 xcd][32 wg][40 rows][16 token slots]    (above 8 tokens: one row per line), or
 //        [8 xcd][32 wg][40 rows][32 token slots]    (above 16 tokens: two lines per row)
@@ -116,6 +117,8 @@ constexpr int kLoRow = kRank + 8;           // padded LDS row of a lo plane (bf1
 //        one replica per consumer XCD, and the blocks are spread 512 bytes
 //        apart: every line is then read by the 32 workgroups of one XCD,
 //        spread over many memory channels, instead of by all 256 at once.
+//        (Measured: a [token][320 rows] layout, whose lines several reducers
+//        write in part, makes hop 2 take 1-2 us longer.)
 constexpr int kLoRows = 4;
 // Per token count: the ssq words of one workgroup (one line, two above 16
 // tokens), the words of a lo block (2 or 4 lines, 8 above 16 tokens).
@@ -357,7 +360,12 @@ __device__ __forceinline__ void tile_lane(int q, int lane, int& row, int& j)
 {
     const int p = 64 * q + lane;
     row = p / RC;
-    const int rem = p - row * RC;
+    // (a separate 24-bit product: fused, the compiler makes it a 64-bit
+    // multiply-add whose unused high addend may sit in a register still being
+    // loaded, and waits for that load)
+    unsigned prod = __umul24((unsigned)row, (unsigned)RC);
+    asm("" : "+v"(prod));
+    const int rem = p - (int)prod;
     j = 8 * line_perm<RC>(row, rem >> 3) + ((rem & 7) ^ swz(row));
 }
 // 16 bytes per lane from memory into LDS: lane l's bytes land at
@@ -365,6 +373,29 @@ __device__ __forceinline__ void tile_lane(int q, int lane, int& row, int& j)
 __device__ __forceinline__ void dma16(const uint16_t* g, uint4* lds_wave_base)
 {
     __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+}
+// LDS stores written as inline asm, which the compiler does not see: it would
+// make a C++ store into the LDS array wait for every load into LDS still in
+// flight (the W_down tile), where these run while the tile lands.  Barriers
+// wait for them (lgkmcnt).
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)p;  // the low 32 bits of a shared-aperture address are the LDS offset
+}
+__device__ __forceinline__ void ds_st32(const void* p, uint32_t v)
+{
+    asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void ds_st64(const void* p, u32x2_t v)
+{
+    asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// The same through a buffer resource: `voff` is the lane's byte offset.  The
+// compiler orders these with ordinary loads (a wait for a load issued before
+// them leaves them in flight), where after global_load_lds it waits for all.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint4* lds_wave_base, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, 0, 0, 0);
 }
 
 // The arguments the first loads need come first: the library is built with
@@ -441,8 +472,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         poisoned_wg = 0;  // (ordered before any setter by the barriers B1, Bc1, Bs)
     const float* const Pm = P ? P : R;  // (a missing pending re-reads R)
 
-    // ---- Loads.  The W_down tile, the activations of its columns and the
-    //      poll-line touches come first; the W_up tile and R' of its rows are
+    // ---- Loads.  The poll-line touches, the activations of the W_down tile's
+    //      columns and the tile come first; the W_up tile and R' of its rows are
     //      issued only after this workgroup's down work (and, for a reducer,
     //      after hop 1).  While loads into LDS are in flight the compiler makes
     //      every LDS access wait for them, and a CU answers a poll only after
@@ -450,27 +481,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     //      either.  Loads issued before the first wait are unconditional
     //      (items past the end re-read item 0): a conditional load makes the
     //      compiler merge registers, which waits.
-    // (1) W_down tile: rows 40 x + row, columns k0 + 8 j ..
-    for (int q = wave; q < kTileInstr; q += 8) {
-        int row, j;
-        tile_lane<kRowChunks>(q, lane, row, j);
-        dma16(W_down + (size_t)(kDecRowsPerXcd * x + row) * kD + k0 + 8 * j, dtile + 64 * q);
-    }
-    // (2) the activations of columns [k0, k0 + 320)
-    constexpr int kItems = kStageItems * T;
-    constexpr int kPasses = (kItems + kDecThreads - 1) / kDecThreads;
-    float4 rv[kPasses], pv[kPasses], wv[kPasses];
-#pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-        const int it = threadIdx.x + kDecThreads * pass;
-        const int itc = it < kItems ? it : 0;
-        const int at = itc / kStageItems, f = itc - at * kStageItems;
-        const size_t o = (size_t)at * kD + k0 + 4 * f;
-        rv[pass] = *reinterpret_cast<const float4*>(R + o);
-        pv[pass] = *reinterpret_cast<const float4*>(Pm + o);
-        wv[pass] = *reinterpret_cast<const float4*>(w_norm + k0 + 4 * f);
-    }
-    // (3) a reducer touches (plain loads, which keep the lines in this XCD's
+    // (0) a reducer touches (plain loads, which keep the lines in this XCD's
     //     L2) the lines it will poll: the 32 producers' partial rows 3 u ..
     //     3 u + 2 and their sums of squares.  Polls then hit L2 and see a
     //     producer's store as soon as it lands, instead of each round
@@ -503,6 +514,42 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             touched2 = *reinterpret_cast<const uint32_t*>(la + 16);
             touched3 = *reinterpret_cast<const uint32_t*>(lb);
             touched4 = *reinterpret_cast<const uint32_t*>(lb + 16);
+        }
+    }
+    // (1) the activations of columns [k0, k0 + 320), first: staging y waits
+    //     only for them and runs while the W_down tile lands
+    constexpr int kItems = kStageItems * T;
+    constexpr int kPasses = (kItems + kDecThreads - 1) / kDecThreads;
+    float4 rv[kPasses], pv[kPasses], wv[kPasses];
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int it = threadIdx.x + kDecThreads * pass;
+        const int itc = it < kItems ? it : 0;
+        const int at = itc / kStageItems, f = itc - at * kStageItems;
+        const size_t o = (size_t)at * kD + k0 + 4 * f;
+        rv[pass] = *reinterpret_cast<const float4*>(R + o);
+        pv[pass] = *reinterpret_cast<const float4*>(Pm + o);
+        wv[pass] = *reinterpret_cast<const float4*>(w_norm + k0 + 4 * f);
+    }
+    // (2) W_down tile: rows 40 x + row, columns k0 + 8 j .. (buffer loads
+    //     into LDS, which the compiler counts like ordinary loads; the
+    //     scheduling barrier keeps them behind the activations)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const __amdgpu_buffer_rsrc_t wdr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(W_down), 0, 0x7fffffff, 0x00020000);
+        // instructions wave + 8 k: k < 3 in every wave, k = 3 in wave 0 only
+        // (unrolled, and unconditional where possible: the compiler can then
+        // count the loads issued after the activations)
+        static_assert(kTileInstr == 25, "25 wave instructions per tile");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = wave + 8 * k;
+            if (k < 3 || wave == 0) {
+                int row, j;
+                tile_lane<kRowChunks>(q, lane, row, j);
+                bdma16(wdr, dtile + 64 * q, 2u * ((uint32_t)(kDecRowsPerXcd * x + row) * kD + k0 + 8 * j));
+            }
         }
     }
     // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
@@ -561,11 +608,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 ss += r * r;
                 split3(r * wvv[e], hi[e], mi[e], lo[e]);
             }
-            sspart[at * kStageItems + f] = ss;
+            ds_st32(&sspart[at * kStageItems + f], __float_as_uint(ss));
             const int col = 4 * f;
-            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(0, at) * kYRow + col]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(1, at) * kYRow + col]) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-            *reinterpret_cast<uint2*>(&ypl[plane_row<T>(2, at) * kYRow + col]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            ds_st64(&ypl[plane_row<T>(0, at) * kYRow + col], u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+            ds_st64(&ypl[plane_row<T>(1, at) * kYRow + col], u32x2_t{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16)});
+            ds_st64(&ypl[plane_row<T>(2, at) * kYRow + col], u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
         }
     }
     wait_all_loads();  // this wave's part of the W_down tile is in LDS
