@@ -466,6 +466,222 @@ __global__ __launch_bounds__(kDnWaves * 64) void prefill_down(int T, const float
 }
 
 // ---------------------------------------------------------------------------
+// P1 for short chunks (at most kSmMaxTok tokens; 80 splits of 128 columns).
+// The 128-token kernel above needs one memory latency per K step and runs 80
+// workgroups for such chunks; this one issues every load at entry and spreads
+// the chunk over 80 x NT workgroups.  Workgroup b = 8 i + x (XCD x) takes
+// split 10 x + i / NT and token tile i % NT of TT tokens: the NT tiles of a
+// split are dispatched together on one XCD, so its 80 KB W_down slice comes
+// from memory once.
+//  * loads: the tile's R (+ pending) and w_norm columns into registers, then
+//    the whole W_down slice (320 rows x 128 columns) into LDS as whole
+//    128-byte lines, the first line of every row (K steps 0-1) before the
+//    second (K steps 2-3): [2 lines][320 rows][8 chunks], chunk c of a line
+//    at slot c ^ swz8(row);
+//  * y = R' * w_norm split into 3 bf16 planes [3][TT tokens][16 chunks] in LDS
+//    (chunk j of token r at line_pos16(r, j)) with the tokens' sums of
+//    squares, while the slice lands;
+//  * 8 waves of MFMAs: wave w takes tokens 16 (w % NTH) .. +15 and rows
+//    RW (w / NTH) .. +RW-1 (NTH = TT / 16 token groups, RW = 320 NTH / 8),
+//    A = W_down rows, B = one y plane per piece: K steps 0-1 once the first
+//    lines have landed, 2-3 after the second; lane (n, g) ends with rows
+//    4 g .. 4 g + 3 of each 16-row block for token n in three accumulators
+//    and stores hi + (mid + lo3) as partial dots, block by block while the
+//    next block's products run.
+// ---------------------------------------------------------------------------
+constexpr int kSmSplits = 80;
+constexpr int kSmCols = kD / kSmSplits;     // 128
+constexpr int kSmRowChunks = kSmCols / 8;   // 16 chunks of 8 bf16 per row
+constexpr int kSmWChunks = kRank * kSmRowChunks;  // 5120 (80 KB)
+constexpr int kSmMaxTok = 192;
+
+// Position (in chunks) of chunk j (0..15) of row r in a block of 16-chunk
+// rows: chunks are swizzled inside their 128-byte line and odd rows swap the
+// two lines, so 8 lanes reading chunk j of 8 consecutive rows hit 8 distinct
+// 16-byte bank groups.
+__host__ __device__ constexpr int line_pos16(int r, int j)
+{
+    return 16 * r + 8 * ((j >> 3) ^ (r & 1)) + ((j & 7) ^ swz8(r));
+}
+
+template <int TT, bool HAS_P>
+__global__ __launch_bounds__(512) void prefill_down_small(int T, const float* __restrict__ R,
+                                                          const float* __restrict__ P,
+                                                          const float* __restrict__ w_norm,
+                                                          const uint16_t* __restrict__ W_down,
+                                                          float* __restrict__ part, float* __restrict__ ssq)
+{
+    constexpr int NTH = TT / 16;           // token groups of 16
+    constexpr int RW = kRank * NTH / 8;    // rows per wave
+    constexpr int MB = RW / 16;            // 16-row blocks per wave
+    constexpr int NPASS = TT * kSmRowChunks / 512;  // conversion items per thread
+    constexpr int kYChunks = TT * kSmRowChunks;     // one y plane
+    static_assert((TT == 32 || TT == 64) && RW % 16 == 0 && NPASS >= 1, "tiling");
+    static_assert(kSmWChunks % (8 * 64) == 0, "W slice: whole wave instructions per wave");
+    __shared__ __align__(16) uint4 lds[kSmWChunks + 3 * kYChunks];
+    const uint32_t w_lds = lds_addr(lds), y_lds = w_lds + 16 * kSmWChunks;
+
+    const int nt = gridDim.x / kSmSplits;
+    const int b = blockIdx.x, x = b & 7, i = b >> 3;
+    const int sig = 10 * x + i / nt, t0 = (i % nt) * TT;
+    const int kbase = kSmCols * sig;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    // (1) R (+ pending) and w_norm of item it = tid + 512 k: token it / 16,
+    //     columns 8 (it % 16) .. +7 (tokens past T re-read token T - 1)
+    float4 rv[NPASS][2], pv[NPASS][2], wv[2];
+    const int c = tid & 15;
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+        const int tl = (tid >> 4) + 32 * k;
+        const int t = t0 + tl < T ? t0 + tl : T - 1;
+        const float* rp = R + (size_t)t * kD + kbase + 8 * c;
+        rv[k][0] = *reinterpret_cast<const float4*>(rp);
+        rv[k][1] = *reinterpret_cast<const float4*>(rp + 4);
+        if constexpr (HAS_P) {
+            const float* pp = P + (size_t)t * kD + kbase + 8 * c;
+            pv[k][0] = *reinterpret_cast<const float4*>(pp);
+            pv[k][1] = *reinterpret_cast<const float4*>(pp + 4);
+        }
+    }
+    wv[0] = *reinterpret_cast<const float4*>(w_norm + kbase + 8 * c);
+    wv[1] = *reinterpret_cast<const float4*>(w_norm + kbase + 8 * c + 4);
+    // (2) the W_down slice: wave instruction q (0..79) fills LDS positions
+    //     64 q .. 64 q + 63, i.e. line q / 40 of rows 8 (q % 40) .. +7; eight
+    //     consecutive lanes fetch one whole line.  Each wave issues its five
+    //     first-line instructions (k < 5) before its second-line ones.
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const __amdgpu_buffer_rsrc_t wr = rsrc_of(W_down);
+#pragma unroll
+        for (int k = 0; k < kSmWChunks / 512; ++k) {
+            const int q = wave + 8 * k;
+            const int ln = q / 40, row = 8 * (q - 40 * ln) + (lane >> 3);
+            const int j = 8 * ln + ((lane & 7) ^ swz8(row));
+            bdma16(wr, lds + 64 * q, 2u * ((uint32_t)row * kD + kbase + 8 * j), 0);
+        }
+    }
+    // (3) y planes and sums of squares (LDS stores as inline asm: the
+    //     compiler would make them wait for the slice's loads)
+    float ssk[NPASS];
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+        const int tl = (tid >> 4) + 32 * k;
+        const float rr[8] = {rv[k][0].x, rv[k][0].y, rv[k][0].z, rv[k][0].w,
+                             rv[k][1].x, rv[k][1].y, rv[k][1].z, rv[k][1].w};
+        const float ww[8] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w};
+        float pr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_P) {
+            const float q8[8] = {pv[k][0].x, pv[k][0].y, pv[k][0].z, pv[k][0].w,
+                                 pv[k][1].x, pv[k][1].y, pv[k][1].z, pv[k][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pr[e] = q8[e];
+        }
+        float ss = 0.f;
+        uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = HAS_P ? rr[e] + pr[e] : rr[e];
+            ss += xv * xv;
+            split3(xv * ww[e], hi[e], mi[e], lo[e]);
+        }
+        const uint32_t a = y_lds + 16 * line_pos16(tl, c);
+        ds_write16(a, u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)});
+        ds_write16(a + 16 * kYChunks,
+                   u32x4{mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16), mi[4] | (mi[5] << 16), mi[6] | (mi[7] << 16)});
+        ds_write16(a + 32 * kYChunks,
+                   u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)});
+        // the token's 16 lanes (one 16-lane row of the wave) combine theirs
+        ss += __shfl_xor(ss, 8, 16);
+        ss += __shfl_xor(ss, 4, 16);
+        ss += __shfl_xor(ss, 2, 16);
+        ss += __shfl_xor(ss, 1, 16);
+        ssk[k] = ss;  // (stored at the end: no store may sit among the loads the waits count)
+    }
+    ring_barrier<kSmWChunks / 1024>();  // y planes and every wave's first lines in LDS
+
+    // (4) products: wave w, tokens 16 th + n, rows RW rg + 16 mb + 4 g ..
+    const int th = wave % NTH, rg = wave / NTH;
+    const int n = lane & 15, g = lane >> 4;
+    f32x4_t acc[MB][3];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+            acc[mb][pc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto w_at = [&](int row, int j) { return w_lds + 16 * ((j >> 3) * (kRank * 8) + 8 * row + ((j & 7) ^ swz8(row))); };
+    auto y_at = [&](int pc, int j) { return y_lds + 16 * (pc * kYChunks + line_pos16(16 * th + n, j)); };
+    // K steps 0-1 (the first lines)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int j = 4 * ks + g;
+        u32x4 a[MB], bb[3];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            a[mb] = ds_read16(w_at(RW * rg + 16 * mb + n, j));
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+            bb[pc] = ds_read16(y_at(pc, j));
+        lds_wait(a);
+        lds_wait(bb);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc)
+                acc[mb][pc] = mfma16(a[mb], bb[pc], acc[mb][pc]);
+    }
+    ring_barrier<0>();  // every wave's second lines in LDS
+    // K steps 2-3, block by block; the partial dots of block mb - 1 are
+    // stored (written through, sc1: they drain while other workgroups
+    // compute instead of all at the end of the launch from the L2s) while
+    // block mb's products run
+    const int t = t0 + 16 * th + n;
+    const __amdgpu_buffer_rsrc_t prs = rsrc_of(part);
+    const uint32_t dst = 4u * (uint32_t)(((size_t)sig * T + (t < T ? t : 0)) * kRank + RW * rg + 4 * g);
+    auto store_block = [&](int mb) {
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = acc[mb][0][e] + (acc[mb][1][e] + acc[mb][2][e]);
+        if (t < T)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs, dst + 64u * mb, 0, 16 /* sc1 */);
+    };
+    u32x4 b2[2][3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+            b2[h][pc] = ds_read16(y_at(pc, 4 * (2 + h) + g));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        u32x4 a2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a2[h] = ds_read16(w_at(RW * rg + 16 * mb + n, 4 * (2 + h) + g));
+        lds_wait(a2);
+        if (mb == 0) {
+            lds_wait(b2[0]);
+            lds_wait(b2[1]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc)
+                acc[mb][pc] = mfma16(a2[h], b2[h][pc], acc[mb][pc]);
+        if (mb > 0)
+            store_block(mb - 1);
+    }
+    store_block(MB - 1);
+#pragma unroll
+    for (int k = 0; k < NPASS; ++k) {
+        const int tl = (tid >> 4) + 32 * k;
+        if (c == 0 && t0 + tl < T)
+            ssq[(size_t)sig * T + t0 + tl] = ssk[k];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // P2: lo = sum_s rs_s * stream partial (fp32), in the tiled layout P3 copies
 // into LDS verbatim: for token tile u (64 tokens) and K step ks, 64 rows of 32
 // floats (8 KB) at chunk (u * 10 + ks) * 512; chunk c of row r at slot
@@ -476,24 +692,28 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
                                                   const float* __restrict__ ssq, uint4* __restrict__ lo_tiled)
 {
     constexpr int Q = S / 4;  // splits per stream
-    // Fine splits (short chunks, latency-bound): four lanes per (token, chunk
-    // of 4 rank indices), lane s summing stream s's Q partials, combined in
-    // registers.  Coarse splits (long chunks, bandwidth-bound): one lane sums
+    // Fine splits (short chunks, latency-bound): 4 G lanes per (token, chunk
+    // of 4 rank indices), lane (g, s) summing Q / G partials of stream s, the
+    // G groups combined in registers, then the streams (80 splits: G = 4, so
+    // the few workgroups of a short chunk do not each read 160 KB; 32 splits:
+    // G = 1).  Coarse splits (long chunks, bandwidth-bound): one lane sums
     // all four streams.
-    constexpr int L = S >= 32 ? 4 : 1;
+    constexpr int G = S == 80 ? 4 : 1;
+    constexpr int L = S >= 32 ? 4 * G : 1;
+    static_assert(Q % G == 0, "split groups");
     const int idx = (blockIdx.x * 256 + threadIdx.x) / L;
     const int t = idx / (kRank / 4);
     const int c4 = idx - t * (kRank / 4);
     if (t >= Tpad)  // (whole lane groups: Tpad * 80 groups fill whole waves)
         return;
     float lo[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (L == 4) {
-        const int s = threadIdx.x & 3;
+    if constexpr (L >= 4) {
+        const int s = threadIdx.x & 3, qg = (threadIdx.x >> 2) & (G - 1);
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (t < T) {
             float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int q = 0; q < Q; ++q) {
+#pragma unroll 5
+            for (int q = (Q / G) * qg; q < (Q / G) * (qg + 1); ++q) {
                 const int sg = Q * s + q;
                 ss += ssq[(size_t)sg * T + t];
                 const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
@@ -501,6 +721,16 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
                 sum[1] += a.y;
                 sum[2] += a.z;
                 sum[3] += a.w;
+            }
+            if constexpr (G == 4) {
+                // (g0 + g1) + (g2 + g3), the same bits in all four group lanes
+                ss += __shfl_xor(ss, 4);
+                ss += __shfl_xor(ss, 8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sum[e] += __shfl_xor(sum[e], 4);
+                    sum[e] += __shfl_xor(sum[e], 8);
+                }
             }
             const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
 #pragma unroll
@@ -513,7 +743,7 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
             const float a = v[e] + __shfl_xor(v[e], 1);
             lo[e] = a + __shfl_xor(a, 2);
         }
-        if (s != 0)
+        if ((threadIdx.x & (L - 1)) != 0)
             return;
     } else if (t < T) {
         float v[4][4];
@@ -556,9 +786,11 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
 // bf16 pieces.  D then holds, in lane (n, g), token 16 w + n and columns 4 g
 // .. +3 of every stream, so the mix is per lane.  LDS stage (12 KB): W_up
 // panel (64 rows: row 16 s + j = W_up row s * 2560 + c0 + j, 4 KB), then the
-// tile's lo block of the step (8 KB).  Three stages, loaded two steps ahead.
+// tile's lo block of the step (8 KB).  NS stages, loaded NS - 1 steps ahead
+// (each step's work is short next to a memory latency): 3 ahead for a chunk
+// of one token tile, 4 for two, 2 for longer ones.  (Measured at 33 and 64
+// tokens: all 10 steps loaded at entry is 1 us slower than 3 ahead.)
 // ---------------------------------------------------------------------------
-constexpr int kUpSlots = 3;
 
 // Calls f(std::integral_constant<int, K>) for K = K0 .. K0 + N - 1.
 template <int K0, int N, typename F>
@@ -570,7 +802,7 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
-template <bool HAS_P, bool BF16_LO>
+template <bool HAS_P, bool BF16_LO, int NS>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* R,
@@ -587,7 +819,8 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
     constexpr int kUpStage = kUpWChunks + kLoTile;      // 768 chunks
     constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (3)
     constexpr int NB = 2 * CB;                          // panel blocks of two streams
-    __shared__ __align__(16) uint4 lds[kUpSlots * kUpStage];
+    static_assert(NS >= 3 && NS <= kUpSteps, "stages");
+    __shared__ __align__(16) uint4 lds[NS * kUpStage];
 
     const int b = blockIdx.x;
     const int x = b & 7, q = b >> 3;
@@ -684,30 +917,19 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
 
     // The epilogue's R: this lane's token, columns c0 + 16 cb + 4 g .. +3 of
     // every stream (tokens past T re-read token T - 1 and store nothing).
-    // Its 16 loads are issued two steps before the end of the K loop, after
-    // the last stage's loads, and are counted in the waits that follow.
+    // Its loads are issued right after the last stage's loads and are
+    // counted in the waits that follow.
     constexpr int kRLoads = 4 * CB;
     const int t = t0 + lrow;
     const int tr = t < T ? t : T - 1;
     const float* rrow = R + (size_t)tr * kD + c0 + 4 * g;
     float4 rv[CB][4];  // [column block][stream]
 
-    // Step ks: stage ks + 2 is issued (the wait at the end of the step leaves
-    // exactly those loads in flight); the matrix cores run step ks.
-    issue(0, 0);
-    issue(1, 1);
-    ring_barrier<kUpLoads>();
-    int slot = 0;  // slot of step ks
-#pragma unroll 1
-    for (int ks = 0; ks < kUpSteps - 3; ++ks) {
-        issue(ks + 2, slot == 0 ? 2 : slot - 1);  // (ks + 2) % 3
-        compute(slot);
-        ring_barrier<kUpLoads>();
-        slot = slot == 2 ? 0 : slot + 1;
-    }
-    issue(kUpSteps - 1, slot == 0 ? 2 : slot - 1);
-    order();
-    {
+    // Stage k goes into slot k % NS.  Stages 0 .. NS - 2 are issued first;
+    // step ks waits for its stage (and for every wave to be done with step
+    // ks - 1), issues stage ks + NS - 1 into the slot step ks - 1 used, then
+    // runs its MFMAs.  After the last stage come the epilogue's R loads.
+    auto load_r = [&]() {
         // Loads through a pointer the compiler cannot trace to the read-only
         // argument: such loads count as ordinary memory accesses and stay
         // between the surrounding asm statements, where the waits count them.
@@ -721,14 +943,25 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                 const f32x4_t v = rl[(s * kWidth + 16 * cb) / 4];
                 rv[cb][s] = make_float4(v[0], v[1], v[2], v[3]);
             }
-    }
-    compute(slot);
-    ring_barrier<kUpLoads + kRLoads>();
-    slot = slot == 2 ? 0 : slot + 1;
-    compute(slot);
-    ring_barrier<kRLoads>();
-    compute(slot == 2 ? 0 : slot + 1);
-
+    };
+    static_for<0, NS - 1>([&](auto kc) { constexpr int k = decltype(kc)::value; issue(k, k); });
+    static_for<0, kUpSteps>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        // this wave's loads issued after stage ks when the step starts: the
+        // stages up to `last`, and the R loads (issued at step kUpSteps - NS)
+        constexpr int last = ks + NS - 2 < kUpSteps - 1 ? ks + NS - 2 : kUpSteps - 1;
+        constexpr int fly = (last - ks) * kUpLoads + (ks > kUpSteps - NS ? kRLoads : 0);
+        ring_barrier<fly>();
+        if constexpr (ks + NS - 1 < kUpSteps) {
+            order();
+            issue(ks + NS - 1, (ks + NS - 1) % NS);
+            if constexpr (ks + NS - 1 == kUpSteps - 1) {
+                order();
+                load_r();
+            }
+        }
+        compute(ks % NS);
+    });
     // gated = up (identity epilogue); mixed = sum_s gated_s * R'_s, then images.
     if (HAS_P) {
         const float* prow = P + (size_t)tr * kD + c0 + 4 * g;
@@ -1296,7 +1529,7 @@ template <int S>
 void launch_lo(int Tc, int tiles, float* part, float* ssq, uint4* planes, hipStream_t stream)
 {
     const int items = tiles * kTok * (kRank / 4);
-    constexpr int lanes = S >= 32 ? 4 : 1;  // lanes per item (as in prefill_lo)
+    constexpr int lanes = S == 80 ? 16 : (S >= 32 ? 4 : 1);  // lanes per item (as in prefill_lo)
     hipLaunchKernelGGL(prefill_lo<S>, dim3((lanes * items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part,
                        ssq, planes);
 }
@@ -1305,6 +1538,17 @@ template <int S>
 void launch_down_lo(int Tc, int tiles, const float* Rc, const float* Pc, const float* w_norm,
                     const uint16_t* W_down, float* part, float* ssq, uint4* planes, hipStream_t stream)
 {
+    if constexpr (S == kSmSplits) {
+        if (Tc <= kSmMaxTok) {
+            // short chunks: 32-token tiles up to 96 tokens, 64-token ones above
+            const bool t32 = Tc <= 96;
+            const dim3 grid(kSmSplits * ((Tc + (t32 ? 31 : 63)) / (t32 ? 32 : 64))), block(512);
+            auto* dn = Pc ? (t32 ? prefill_down_small<32, true> : prefill_down_small<64, true>)
+                          : (t32 ? prefill_down_small<32, false> : prefill_down_small<64, false>);
+            hipLaunchKernelGGL(dn, grid, block, 0, stream, Tc, Rc, Pc, w_norm, W_down, part, ssq);
+            return launch_lo<S>(Tc, tiles, part, ssq, planes, stream);
+        }
+    }
     const dim3 grid1(S * ((Tc + kDnTok - 1) / kDnTok)), block1(kDnWaves * 64);
     if constexpr (S >= 8) {  // (4 splits are never used with pending)
         if (Pc) {
@@ -1367,8 +1611,15 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
         const bool narrow = tiles <= 4;  // 16-column tiles (measured: better up to 256 tokens)
         if (narrow) {
-            auto* up = Pc ? (bf16_lo ? prefill_upmix<true, true> : prefill_upmix<true, false>)
-                          : (bf16_lo ? prefill_upmix<false, true> : prefill_upmix<false, false>);
+            // ring depth by chunk (measured best): 4 stages for one token tile,
+            // 5 for two, 3 above
+            auto pick = [&](auto ns) {
+                constexpr int NS = decltype(ns)::value;
+                return Pc ? (bf16_lo ? prefill_upmix<true, true, NS> : prefill_upmix<true, false, NS>)
+                          : (bf16_lo ? prefill_upmix<false, true, NS> : prefill_upmix<false, false, NS>);
+            };
+            auto* up = tiles == 1 ? pick(std::integral_constant<int, 4>{})
+                                  : tiles == 2 ? pick(std::integral_constant<int, 5>{}) : pick(std::integral_constant<int, 3>{});
             hipLaunchKernelGGL(up, dim3(4 * 8 * kGroupsPerXcd * tiles), dim3(256), 0, stream, Tc, planes, W_up, Rc,
                                Pc, out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
         } else if (Pc) {

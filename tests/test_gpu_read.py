@@ -268,7 +268,8 @@ def test_lo_is_at_fp32_level(T, pending):
     assert np.max(rel) <= LO_TOL
 
 
-@pytest.mark.parametrize("T, pending", [(100, False), (300, False), (2048, False), (4097, True)])
+@pytest.mark.parametrize("T, pending", [(40, True), (100, False), (180, False), (300, False), (2048, False),
+                                        (4097, True)])
 def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     """hc_read_bf16_lo, stage-wise: the oracle's mode that rounds its exact lo
     to bf16 (nearest even) before the up projection is the reference, held to
@@ -281,7 +282,8 @@ def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     rounding its flagged values the other way could move one of its mixed
     values by more than 1e-6 of max|mixed| (half the tolerance).  The expected
     values are the oracle's alone; the test prints how many tokens it leaves
-    out.  T = 100: 16-column up+mix tiles without pending; T = 300 and 2048:
+    out.  T = 40, 100, 180: 16-column up+mix tiles (one token tile with
+    pending, two and three without: the three ring depths); T = 300 and 2048:
     the persistent up+mix; T = 4097 (two chunks, with pending): the
     per-tile up+mix, a sample of tokens.  The mode
     must also differ from the exact read (the fast path ran)."""
@@ -470,6 +472,22 @@ def test_wide_path_boundaries(T, pending):
              for t in (b - 1, b) if 0 <= t < T}
     toks = np.array(sorted(set(_sample_tokens(T, k=24, seed=T).tolist()) | edges))
     assert_parity(gpu, _oracle(inp, toks), tokens=toks, label="T=%d pending=%s" % (T, pending))
+
+
+@pytest.mark.parametrize("T, pending", [(33, False), (64, False), (96, True), (97, False), (160, True),
+                                        (192, False), (193, True)])
+def test_short_chunk_down_tiles(T, pending):
+    """Chunks of at most 192 tokens run the down projection on 80 x NT
+    workgroups of 32-token tiles (up to 96 tokens) or 64-token tiles (97..192),
+    every load issued at entry; 193 is the first count on the 128-token down
+    kernel.  Both tile sizes with and without pending, ragged last tiles.
+    Full oracle."""
+    _case("short-chunk down tiles: T=%d, pending=%s" % (T, pending))
+    inp = wl.config_inputs(2, T=T, weight_set=9)
+    if not pending:
+        inp.pending = None
+    gpu = hip_read(to_device(inp))
+    assert_parity(gpu, _oracle(inp), label="T=%d pending=%s" % (T, pending))
 
 
 # ---------------------------------------------------------------------------
