@@ -94,9 +94,11 @@ def trace(path: str) -> str:
         cl = _clusters(d)
         for i, c in enumerate(cl):
             tag = "" if len(cl) == 1 else " (size %d of %d)" % (i + 1, len(cl))
-            rows.append((sum(c), "| %s%s | %d | %d | %.3f | %.3f | %.3f | %.3f |" % (
-                name, tag, wgs, len(c), sum(c) / len(c), c[len(c) // 2], c[0], c[-1])))
-    out = ["| kernel | workgroups | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+            p10, p90 = c[(len(c) - 1) // 10], c[(9 * (len(c) - 1)) // 10]  # (nearest rank, lower)
+            rows.append((sum(c), "| %s%s | %d | %d | %.3f | %.3f | %.3f | %.3f | %.3f | %.3f |" % (
+                name, tag, wgs, len(c), sum(c) / len(c), c[len(c) // 2], p10, p90, c[0], c[-1])))
+    out = ["| kernel | workgroups | calls | avg us | median us | p10 us | p90 us | min us | max us |",
+           "|---|---|---|---|---|---|---|---|---|"]
     out += [r for _, r in sorted(rows, key=lambda x: -x[0])]
     return "\n".join(out)
 
