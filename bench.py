@@ -20,7 +20,9 @@ the pending write committed (hc_read_commit) against the read plus a separate
 R += pending, and the prefill read times are reported beside it.  The
 roofline object describes the short-window kernel, next to `stream_floor_us`:
 one launch of that kernel's shape that only streams 13,148,160 bytes (48
-rotated buffers, cold), the floor for a single launch moving the weights.  The
+rotated buffers, cold), the floor for a single launch moving the weights, and
+`launch_floor_us`: the same launch moving 16 bytes, back to back (eager, and
+replayed from a HIP graph), the cost of any launch of that shape.  The
 CPU baseline is the plain oracle on the host, on all its cores (one read per
 core) and on one.  The run prints a hash of the kernel sources it was built
 from, so a profiler run's summary can be tied to the kernels it measured.
@@ -421,6 +423,31 @@ def main():
         del g
     print("# graph us per read by T: %s" % us_graph, file=sys.stderr, flush=True)
     del step_graphs
+
+    # ---- the launch floor: one launch of the same shape that moves 16 bytes,
+    # back to back, eager (bounded by the host's launch rate) and replayed from
+    # a graph of 100 launches (the device's own cost per launch)
+    tiny = torch.zeros(4, dtype=torch.float32, device=dev)
+
+    def tiny_once(s):
+        st = binding.hc_stream_read(tiny, 16, sink, s.cuda_stream)
+        if st != 0:
+            raise binding.HCError(st, "hc_stream_read")
+
+    for _ in range(100):
+        tiny_once(stream)
+    n_tiny, n_tiny_g = (200, 2) if args.light else (2000, 20)
+    ms_tiny = time_region(stream, lambda k: tiny_once(stream), n_tiny)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gstream):
+        for _ in range(100):
+            tiny_once(gstream)
+    with torch.cuda.stream(gstream):
+        g.replay()
+    ms_tiny_g = time_region(gstream, lambda k: g.replay(), n_tiny_g)
+    del g
+    launch_floor = {"eager": round(ms_tiny * 1e3 / n_tiny, 3), "graph": round(ms_tiny_g * 1e3 / (100 * n_tiny_g), 3)}
+    print("# launch floor (16 bytes per launch): %s us" % launch_floor, file=sys.stderr, flush=True)
     timeouts += binding.hc_timeouts(stream) + binding.hc_timeouts(gstream)
     if timeouts:
         print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
@@ -460,6 +487,7 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "stream_floor_us": floor_us,
+        "launch_floor_us": launch_floor,
         "timeouts": timeouts,
         "kernel_source_hash": src_hash,
     }

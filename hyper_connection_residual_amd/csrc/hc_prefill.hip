@@ -692,29 +692,32 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
                                                   const float* __restrict__ ssq, uint4* __restrict__ lo_tiled)
 {
     constexpr int Q = S / 4;  // splits per stream
-    // Fine splits (short chunks, latency-bound): 4 G lanes per (token, chunk
-    // of 4 rank indices), lane (g, s) summing Q / G partials of stream s, the
-    // G groups combined in registers, then the streams (80 splits: G = 4, so
-    // the few workgroups of a short chunk do not each read 160 KB; 32 splits:
-    // G = 1).  Coarse splits (long chunks, bandwidth-bound): one lane sums
-    // all four streams.
-    constexpr int G = S == 80 ? 4 : 1;
-    constexpr int L = S >= 32 ? 4 * G : 1;
-    static_assert(Q % G == 0, "split groups");
-    const int idx = (blockIdx.x * 256 + threadIdx.x) / L;
-    const int t = idx / (kRank / 4);
-    const int c4 = idx - t * (kRank / 4);
-    if (t >= Tpad)  // (whole lane groups: Tpad * 80 groups fill whole waves)
-        return;
-    float lo[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (L >= 4) {
-        const int s = threadIdx.x & 3, qg = (threadIdx.x >> 2) & (G - 1);
+    auto store = [&](int t, int c4, const float (&lo)[4]) {
+        const int tile = t / kTok, tl = t - tile * kTok;
+        const int ks = c4 >> 3, c = c4 & 7;
+        lo_tiled[(size_t)(tile * kUpSteps + ks) * kLoTile + 8 * tl + (c ^ swz8(tl))] =
+            make_uint4(__float_as_uint(lo[0]), __float_as_uint(lo[1]), __float_as_uint(lo[2]), __float_as_uint(lo[3]));
+    };
+    if constexpr (S == 80) {
+        // 80 splits (short chunks, latency-bound): one wave per (token, block
+        // rb of 32 rank indices).  Lane (s, h, c) sums partials 10 h .. 10 h +
+        // 9 of stream s for rank indices 4 (8 rb + c) .. +3, so the eight lanes
+        // of a (stream, half) read one whole 128-byte line of each partial row;
+        // the halves are combined, then the streams as (s0 + s1) + (s2 + s3).
+        // (16 lanes per item reading half lines took 1.2 us longer at 64
+        // tokens.)
+        const int wv = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
+        const int t = wv / (kRank / 32), rb = wv - t * (kRank / 32);
+        if (t >= Tpad)  // (whole waves)
+            return;
+        const int ln = threadIdx.x & 63, c = ln & 7, h = (ln >> 3) & 1, s = ln >> 4;
+        const int c4 = 8 * rb + c;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (t < T) {
             float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 5
-            for (int q = (Q / G) * qg; q < (Q / G) * (qg + 1); ++q) {
-                const int sg = Q * s + q;
+#pragma unroll
+            for (int q = 0; q < Q / 2; ++q) {
+                const int sg = Q * s + (Q / 2) * h + q;
                 ss += ssq[(size_t)sg * T + t];
                 const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
                 sum[0] += a.x;
@@ -722,15 +725,51 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
                 sum[2] += a.z;
                 sum[3] += a.w;
             }
-            if constexpr (G == 4) {
-                // (g0 + g1) + (g2 + g3), the same bits in all four group lanes
-                ss += __shfl_xor(ss, 4);
-                ss += __shfl_xor(ss, 8);
+            // h0 + h1, the same bits in both halves' lanes
+            ss += __shfl_xor(ss, 8);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sum[e] += __shfl_xor(sum[e], 4);
-                    sum[e] += __shfl_xor(sum[e], 8);
-                }
+            for (int e = 0; e < 4; ++e)
+                sum[e] += __shfl_xor(sum[e], 8);
+            const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = sum[e] * rs;
+        }
+        float lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = v[e] + __shfl_xor(v[e], 16);
+            lo[e] = a + __shfl_xor(a, 32);
+        }
+        if (ln < 8)
+            store(t, c4, lo);
+        return;
+    }
+    // 32 splits: four lanes per (token, chunk of 4 rank indices), lane s
+    // summing the Q partials of stream s, the streams combined in registers.
+    // Coarse splits (long chunks, bandwidth-bound): one lane sums all four
+    // streams.
+    constexpr int L = S >= 32 ? 4 : 1;
+    const int idx = (blockIdx.x * 256 + threadIdx.x) / L;
+    const int t = idx / (kRank / 4);
+    const int c4 = idx - t * (kRank / 4);
+    if (t >= Tpad)  // (whole lane groups: Tpad * 80 groups fill whole waves)
+        return;
+    float lo[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (L == 4) {
+        const int s = threadIdx.x & 3;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < T) {
+            float ss = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int sg = Q * s + q;
+                ss += ssq[(size_t)sg * T + t];
+                const float4 a = *reinterpret_cast<const float4*>(part + ((size_t)sg * T + t) * kRank + 4 * c4);
+                sum[0] += a.x;
+                sum[1] += a.y;
+                sum[2] += a.z;
+                sum[3] += a.w;
             }
             const float rs = rsqrtf(ss * (1.0f / (float)kWidth) + kEps);
 #pragma unroll
@@ -743,7 +782,7 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
             const float a = v[e] + __shfl_xor(v[e], 1);
             lo[e] = a + __shfl_xor(a, 2);
         }
-        if ((threadIdx.x & (L - 1)) != 0)
+        if ((threadIdx.x & 3) != 0)
             return;
     } else if (t < T) {
         float v[4][4];
@@ -769,10 +808,7 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
         for (int e = 0; e < 4; ++e)
             lo[e] = (v[0][e] + v[1][e]) + (v[2][e] + v[3][e]);
     }
-    const int tile = t / kTok, tl = t - tile * kTok;
-    const int ks = c4 >> 3, c = c4 & 7;
-    lo_tiled[(size_t)(tile * kUpSteps + ks) * kLoTile + 8 * tl + (c ^ swz8(tl))] =
-        make_uint4(__float_as_uint(lo[0]), __float_as_uint(lo[1]), __float_as_uint(lo[2]), __float_as_uint(lo[3]));
+    store(t, c4, lo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1529,7 +1565,7 @@ template <int S>
 void launch_lo(int Tc, int tiles, float* part, float* ssq, uint4* planes, hipStream_t stream)
 {
     const int items = tiles * kTok * (kRank / 4);
-    constexpr int lanes = S == 80 ? 16 : (S >= 32 ? 4 : 1);  // lanes per item (as in prefill_lo)
+    constexpr int lanes = S == 80 ? 8 : (S >= 32 ? 4 : 1);  // lanes per item (as in prefill_lo)
     hipLaunchKernelGGL(prefill_lo<S>, dim3((lanes * items + 255) / 256), dim3(256), 0, stream, Tc, tiles * kTok, part,
                        ssq, planes);
 }
