@@ -64,6 +64,9 @@ def parse():
                          "HBM byte counters of a profiler run)")
     ap.add_argument("--light", action="store_true",
                     help="fewer reads per timing loop (for profiler runs that serialize every dispatch)")
+    ap.add_argument("--no-launch-floor", action="store_true",
+                    help="skip the 16-byte launches of the launch floor (profiler runs: they share the "
+                         "streaming reference's kernel and grid, so a summary could not tell them apart)")
     ap.add_argument("--cpu-cores", type=int, default=0,
                     help="host cores for the all-core oracle leg (0: all, at most 16)")
     ap.add_argument("--traffic-md", default=os.path.join(ROOT, "profiles", "decode_sweep_and_wide_reads_counters.md"),
@@ -427,27 +430,30 @@ def main():
     # ---- the launch floor: one launch of the same shape that moves 16 bytes,
     # back to back, eager (bounded by the host's launch rate) and replayed from
     # a graph of 100 launches (the device's own cost per launch)
-    tiny = torch.zeros(4, dtype=torch.float32, device=dev)
+    launch_floor = None
+    if not args.no_launch_floor:
+        tiny = torch.zeros(4, dtype=torch.float32, device=dev)
 
-    def tiny_once(s):
-        st = binding.hc_stream_read(tiny, 16, sink, s.cuda_stream)
-        if st != 0:
-            raise binding.HCError(st, "hc_stream_read")
+        def tiny_once(s):
+            st = binding.hc_stream_read(tiny, 16, sink, s.cuda_stream)
+            if st != 0:
+                raise binding.HCError(st, "hc_stream_read")
 
-    for _ in range(100):
-        tiny_once(stream)
-    n_tiny, n_tiny_g = (200, 2) if args.light else (2000, 20)
-    ms_tiny = time_region(stream, lambda k: tiny_once(stream), n_tiny)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=gstream):
         for _ in range(100):
-            tiny_once(gstream)
-    with torch.cuda.stream(gstream):
-        g.replay()
-    ms_tiny_g = time_region(gstream, lambda k: g.replay(), n_tiny_g)
-    del g
-    launch_floor = {"eager": round(ms_tiny * 1e3 / n_tiny, 3), "graph": round(ms_tiny_g * 1e3 / (100 * n_tiny_g), 3)}
-    print("# launch floor (16 bytes per launch): %s us" % launch_floor, file=sys.stderr, flush=True)
+            tiny_once(stream)
+        n_tiny, n_tiny_g = (200, 2) if args.light else (2000, 20)
+        ms_tiny = time_region(stream, lambda k: tiny_once(stream), n_tiny)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for _ in range(100):
+                tiny_once(gstream)
+        with torch.cuda.stream(gstream):
+            g.replay()
+        ms_tiny_g = time_region(gstream, lambda k: g.replay(), n_tiny_g)
+        del g
+        launch_floor = {"eager": round(ms_tiny * 1e3 / n_tiny, 3),
+                        "graph": round(ms_tiny_g * 1e3 / (100 * n_tiny_g), 3)}
+        print("# launch floor (16 bytes per launch): %s us" % launch_floor, file=sys.stderr, flush=True)
     timeouts += binding.hc_timeouts(stream) + binding.hc_timeouts(gstream)
     if timeouts:
         print("# WARNING: %d bounded waits expired" % timeouts, file=sys.stderr)
