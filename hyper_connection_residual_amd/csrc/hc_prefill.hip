@@ -813,19 +813,20 @@ __global__ __launch_bounds__(256) void prefill_lo(int T, int Tpad, const float* 
 
 // ---------------------------------------------------------------------------
 // P3 for chunks of at most 4 token tiles: up projection with the stream mix
-// as its epilogue on tiles of 64 tokens x 16 columns x 4 streams, 160
-// workgroups per token tile, each streaming a quarter of a 64-column W_up
-// panel, so a short read loads W_up over most of the chip.  Workgroup b: XCD
-// x = b % 8, q = b / 8: token tile q / 20, column group x + 8 (q % 20).  Wave
-// w owns tokens 16 w .. 16 w + 15 of the tile: MFMA A = W_up rows (4
-// streams), B = lo of the wave's tokens, split in registers into its three
-// bf16 pieces.  D then holds, in lane (n, g), token 16 w + n and columns 4 g
-// .. +3 of every stream, so the mix is per lane.  LDS stage (12 KB): W_up
-// panel (64 rows: row 16 s + j = W_up row s * 2560 + c0 + j, 4 KB), then the
+// as its epilogue on tiles of 64 tokens x 16 CB columns x 4 streams, 160 / CB
+// workgroups per token tile, each streaming a part of a 64-column W_up
+// panel, so a short read loads W_up over most of the chip (CB = 1 for one or
+// two token tiles, 2 for three or four).  Workgroup b: XCD x = b % 8, q = b /
+// 8: token tile q / G, column group x + 8 (q % G), G = 20 / CB.  Wave w owns
+// tokens 16 w .. 16 w + 15 of the tile: MFMA A = W_up rows (4 streams), B =
+// lo of the wave's tokens, split in registers into its three bf16 pieces.  D
+// then holds, in lane (n, g), token 16 w + n and columns 16 cb + 4 g .. +3 of
+// every stream, so the mix is per lane.  LDS stage: the W_up panel (64 CB
+// rows: row 16 CB s + j = W_up row s * 2560 + c0 + j, 4 CB KB), then the
 // tile's lo block of the step (8 KB).  NS stages, loaded NS - 1 steps ahead
 // (each step's work is short next to a memory latency): 3 ahead for a chunk
-// of one token tile, 4 for two, 2 for longer ones.  (Measured at 33 and 64
-// tokens: all 10 steps loaded at entry is 1 us slower than 3 ahead.)
+// of one token tile, 4 for two, 2 for three and 3 for four.  (Measured at 33
+// and 64 tokens: all 10 steps loaded at entry is 1 us slower than 3 ahead.)
 // ---------------------------------------------------------------------------
 
 // Calls f(std::integral_constant<int, K>) for K = K0 .. K0 + N - 1.
@@ -838,7 +839,7 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
-template <bool HAS_P, bool BF16_LO, int NS>
+template <bool HAS_P, bool BF16_LO, int NS, int CB>
 __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __restrict__ lo_tiled,
                                                         const uint16_t* __restrict__ W_up,
                                                         const float* R,
@@ -848,14 +849,13 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                                                         uint16_t* __restrict__ out_fp16,
                                                         float* R_commit)
 {
-    constexpr int CB = 1;                               // column blocks of 16
     constexpr int kCols = 16 * CB;                      // output columns of the tile
-    constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (20)
-    constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 256 chunks
+    constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (20 / CB)
+    constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 256 CB chunks
     constexpr int kUpStage = kUpWChunks + kLoTile;      // 768 chunks
-    constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (3)
+    constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (2 + CB)
     constexpr int NB = 2 * CB;                          // panel blocks of two streams
-    static_assert(NS >= 3 && NS <= kUpSteps, "stages");
+    static_assert(NS >= 3 && NS <= kUpSteps && (CB == 1 || CB == 2), "stages, column blocks");
     __shared__ __align__(16) uint4 lds[NS * kUpStage];
 
     const int b = blockIdx.x;
@@ -1023,27 +1023,30 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
                     *reinterpret_cast<float4*>(crow + s * kWidth + 16 * cb) = rv[cb][s];
         }
     }
-    // 16 columns: lane (n, g) holds token t, columns c0 + 4 g .. +3 of
-    // every stream; the 4 lanes of a token store 64 contiguous bytes
-    const float r[4][4] = {{rv[0][0].x, rv[0][0].y, rv[0][0].z, rv[0][0].w},
-                           {rv[0][1].x, rv[0][1].y, rv[0][1].z, rv[0][1].w},
-                           {rv[0][2].x, rv[0][2].y, rv[0][2].z, rv[0][2].w},
-                           {rv[0][3].x, rv[0][3].y, rv[0][3].z, rv[0][3].w}};
-    float m[4];
+    // lane (n, g) holds token t, columns c0 + 16 cb + 4 g .. +3 of every
+    // stream; the 4 lanes of a token store 64 contiguous bytes per block
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        m[i] = (acc[0][0][i] * r[0][i] + acc[0][1][i] * r[1][i]) + (acc[0][2][i] * r[2][i] + acc[0][3][i] * r[3][i]);
-    if (t < T) {
-        const size_t o = (size_t)t * kWidth + c0 + 4 * g;
-        *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
-        uint32_t bh[4], hh[4];
+    for (int cb = 0; cb < CB; ++cb) {
+        const float r[4][4] = {{rv[cb][0].x, rv[cb][0].y, rv[cb][0].z, rv[cb][0].w},
+                               {rv[cb][1].x, rv[cb][1].y, rv[cb][1].z, rv[cb][1].w},
+                               {rv[cb][2].x, rv[cb][2].y, rv[cb][2].z, rv[cb][2].w},
+                               {rv[cb][3].x, rv[cb][3].y, rv[cb][3].z, rv[cb][3].w}};
+        float m[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
-            hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
+        for (int i = 0; i < 4; ++i)
+            m[i] = (acc[cb][0][i] * r[0][i] + acc[cb][1][i] * r[1][i]) + (acc[cb][2][i] * r[2][i] + acc[cb][3][i] * r[3][i]);
+        if (t < T) {
+            const size_t o = (size_t)t * kWidth + c0 + 16 * cb + 4 * g;
+            *reinterpret_cast<float4*>(out_mixed + o) = make_float4(m[0], m[1], m[2], m[3]);
+            uint32_t bh[4], hh[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bh[i] = __builtin_bit_cast(uint16_t, (__bf16)m[i]);
+                hh[i] = __builtin_bit_cast(uint16_t, (_Float16)m[i]);
+            }
+            *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
+            *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
         }
-        *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16));
-        *reinterpret_cast<uint2*>(out_fp16 + o) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
     }
 }
 
@@ -1645,18 +1648,24 @@ hipError_t launch_prefill(int64_t T, const float* R, const float* P, const float
         if (e != hipSuccess)
             return e;
         float* Cc = R_commit && Pc ? R_commit + in_off : nullptr;
-        const bool narrow = tiles <= 4;  // 16-column tiles (measured: better up to 256 tokens)
+        const bool narrow = tiles <= 4;  // 16- or 32-column tiles (measured: better up to 256 tokens)
         if (narrow) {
-            // ring depth by chunk (measured best): 4 stages for one token tile,
-            // 5 for two, 3 above
-            auto pick = [&](auto ns) {
-                constexpr int NS = decltype(ns)::value;
-                return Pc ? (bf16_lo ? prefill_upmix<true, true, NS> : prefill_upmix<true, false, NS>)
-                          : (bf16_lo ? prefill_upmix<false, true, NS> : prefill_upmix<false, false, NS>);
+            // column blocks and ring depth by chunk (measured best): 16 columns
+            // with 4 stages for one token tile and 5 for two; 32 columns with 3
+            // stages for three tiles and 4 for four
+            auto pick = [&](auto ns, auto cb) {
+                constexpr int NS = decltype(ns)::value, CB = decltype(cb)::value;
+                return Pc ? (bf16_lo ? prefill_upmix<true, true, NS, CB> : prefill_upmix<true, false, NS, CB>)
+                          : (bf16_lo ? prefill_upmix<false, true, NS, CB> : prefill_upmix<false, false, NS, CB>);
             };
-            auto* up = tiles == 1 ? pick(std::integral_constant<int, 4>{})
-                                  : tiles == 2 ? pick(std::integral_constant<int, 5>{}) : pick(std::integral_constant<int, 3>{});
-            hipLaunchKernelGGL(up, dim3(4 * 8 * kGroupsPerXcd * tiles), dim3(256), 0, stream, Tc, planes, W_up, Rc,
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            using I3 = std::integral_constant<int, 3>;
+            using I4 = std::integral_constant<int, 4>;
+            using I5 = std::integral_constant<int, 5>;
+            auto* up = tiles == 1 ? pick(I4{}, I1{}) : tiles == 2 ? pick(I5{}, I1{}) : tiles == 3 ? pick(I3{}, I2{}) : pick(I4{}, I2{});
+            const int cb = tiles <= 2 ? 1 : 2;
+            hipLaunchKernelGGL(up, dim3(8 * (kWidth / (16 * cb) / 8) * tiles), dim3(256), 0, stream, Tc, planes, W_up, Rc,
                                Pc, out_mixed + out_off, out_bf16 + out_off, out_fp16 + out_off, Cc);
         } else if (Pc) {
             auto* up = bf16_lo ? prefill_upmix2<true, true> : prefill_upmix2<true, false>;

@@ -268,7 +268,8 @@ def test_lo_is_at_fp32_level(T, pending):
     assert np.max(rel) <= LO_TOL
 
 
-@pytest.mark.parametrize("T, pending", [(40, True), (100, False), (180, False), (300, False), (2048, False),
+@pytest.mark.parametrize("T, pending", [(40, True), (60, False), (100, False), (120, True), (150, True),
+                                        (180, False), (230, False), (240, True), (300, False), (2048, False),
                                         (4097, True)])
 def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     """hc_read_bf16_lo, stage-wise: the oracle's mode that rounds its exact lo
@@ -282,8 +283,9 @@ def test_bf16_lo_mode_against_the_oracle_fed_bf16_lo(T, pending):
     rounding its flagged values the other way could move one of its mixed
     values by more than 1e-6 of max|mixed| (half the tolerance).  The expected
     values are the oracle's alone; the test prints how many tokens it leaves
-    out.  T = 40, 100, 180: 16-column up+mix tiles (one token tile with
-    pending, two and three without: the three ring depths); T = 300 and 2048:
+    out.  T = 40, 60, 100, 120: 16-column up+mix tiles (one and two token
+    tiles, with and without pending); T = 150, 180, 230, 240: 32-column tiles
+    (three and four token tiles, with and without pending); T = 300 and 2048:
     the persistent up+mix; T = 4097 (two chunks, with pending): the
     per-tile up+mix, a sample of tokens.  The mode
     must also differ from the exact read (the fast path ran)."""
@@ -456,8 +458,8 @@ def test_full_size_config5_every_tile():
                                         (8192, True), (8193, False)])
 def test_wide_path_boundaries(T, pending):
     """Token counts at the wide path's internal boundaries: one token past a
-    128-token down tile; the up+mix tile changes from 16 to 64 columns after
-    256 tokens (4 token tiles); the down projection's K-split count changes
+    128-token down tile; the up+mix tile changes from 16 to 32 columns after
+    128 tokens and to 64 after 256 (4 token tiles); the down projection's K-split count changes
     from 80 (128-column splits) to 32 after 384 tokens, to 16 (stream
     quarters) after 1024, to 8 (stream halves) after 3968 and, without
     pending, to 4 (whole streams) after 8064; one token past an 8192-token
@@ -475,13 +477,14 @@ def test_wide_path_boundaries(T, pending):
 
 
 @pytest.mark.parametrize("T, pending", [(33, False), (64, False), (96, True), (97, False), (160, True),
-                                        (192, False), (193, True)])
+                                        (192, False), (193, True), (250, False)])
 def test_short_chunk_down_tiles(T, pending):
     """Chunks of at most 192 tokens run the down projection on 80 x NT
     workgroups of 32-token tiles (up to 96 tokens) or 64-token tiles (97..192),
     every load issued at entry; 193 is the first count on the 128-token down
-    kernel.  Both tile sizes with and without pending, ragged last tiles.
-    Full oracle."""
+    kernel.  Both tile sizes with and without pending, ragged last tiles.  The
+    up+mix of these chunks: 16-column tiles for one and two token tiles,
+    32-column tiles for three (160, 192) and four (193, 250).  Full oracle."""
     _case("short-chunk down tiles: T=%d, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=9)
     if not pending:
