@@ -242,9 +242,12 @@ def main():
     del floor_bufs
 
     # ---- reads of 9..512 tokens (up to 32: one short-window launch; beyond:
-    # the wide path), eager, weights rotated over the 48 sets
+    # the wide path), eager, weights rotated over the 48 sets.  Every input
+    # is made first, and the reads run after WARM_STEP_MS of GPU time of
+    # window reads, so that no host-side pause between two token counts
+    # lets the engine clock drop before a timing.
     from hyper_connection_residual_amd import workloads as wl
-    us_windows = {}
+    window_inputs = {}
     for T in WINDOWS:
         rng = np.random.default_rng((1, 2000 + T))
         R = torch.from_numpy(wl._normal_residual(rng, T, wl.N_STREAMS, wl.WIDTH)).cuda()
@@ -252,17 +255,22 @@ def main():
         o = (torch.empty((T, 2560), dtype=torch.float32, device=dev),
              torch.empty((T, 2560), dtype=torch.int16, device=dev),
              torch.empty((T, 2560), dtype=torch.int16, device=dev))
+        window_inputs[T] = (R, P, o)
 
-        def window_read(k, T=T, R=R, P=P, o=o):
-            ws = sets[k % N_SETS]
-            st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2],
-                                 stream.cuda_stream)
-            if st != 0:
-                raise binding.HCError(st, "hc_read")
+    def window_read(k, T):
+        R, P, o = window_inputs[T]
+        ws = sets[k % N_SETS]
+        st = binding.hc_read(T, R, P, ws["w_norm"], ws["W_down"], ws["W_up"], o[0], o[1], o[2],
+                             stream.cuda_stream)
+        if st != 0:
+            raise binding.HCError(st, "hc_read")
 
+    warm_windows = warm_steps(stream, lambda k: window_read(k, WINDOWS[k % len(WINDOWS)]))
+    us_windows = {}
+    for T in WINDOWS:
         for k in range(8):
-            window_read(k)
-        ms = time_region(stream, window_read, n_win)
+            window_read(k, T)
+        ms = time_region(stream, lambda k, T=T: window_read(k, T), n_win)
         us_windows[str(T)] = round(ms * 1e3 / n_win, 3)
     print("# windows above 8 tokens, us per read: %s" % us_windows, file=sys.stderr, flush=True)
 
@@ -470,7 +478,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_run": {"eager": warm_eager, "graph": warm_graph},
+        "warmup_run": {"eager": warm_eager, "windows": warm_windows, "graph": warm_graph},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
