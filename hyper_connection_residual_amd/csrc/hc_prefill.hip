@@ -13,7 +13,9 @@
 //             for chunks of more than 8064 tokens without pending, 8 (stream
 //             halves, 1280 columns) from 3969 tokens, 16 (quarters) for
 //             chunks of 1025..3968 tokens, 32 (320 columns) for 385..1024 and
-//             80 (128 columns) up to 384 tokens (splits_for).
+//             80 (128 columns) up to 384 tokens (splits_for).  Chunks of at
+//             most 192 tokens run it on prefill_down_small (80 x NT
+//             workgroups of 32- or 64-token tiles, every load at entry).
 //   P2 lo:    rs[t][s] = 1/sqrt(sum of stream s's split ssq / 2560 + eps) and
 //             lo[t][j] = sum_s rs[t][s] * (stream s's split partials), stored
 //             in fp32 in the tiled layout P3 copies into LDS verbatim (P3
@@ -21,6 +23,7 @@
 //   P3 up+mix: the up projection (K = 320) on the matrix cores, then the mix
 //             of the 4 streams with R' and the bf16 / fp16 images, all in
 //             registers.  Chunks of at most 256 tokens: 16-column tiles
+//             for one or two token tiles, 32-column ones for three or four
 //             (prefill_upmix).  Longer chunks: 128 tokens x 64 columns x 4
 //             streams per workgroup of 8 waves, persistent over its items
 //             without pending (prefill_upmix3), one item per workgroup with
@@ -33,9 +36,9 @@
 // * Weight operands (and P3's lo tiles, and P1's raw activations) go from
 //   memory straight into LDS (16 bytes a lane, global_load_lds_dwordx4 or
 //   its buffer form) through rings: P1 loads its W_down panel one K step of
-//   32 ahead and raw R (and pending) two or three steps ahead; the 16-column
-//   P3 runs a three-stage ring two steps ahead, the 128-token ones a
-//   five-stage ring four steps ahead.  LDS is read with inline-asm
+//   32 ahead and raw R (and pending) two or three steps ahead; the narrow
+//   P3 runs a ring of three to five stages (two to four steps ahead), the
+//   128-token ones a five-stage ring four steps ahead.  LDS is read with inline-asm
 //   ds_read_b128 and every wait is explicit: the compiler, seeing an LDS read
 //   that may alias a load still landing in LDS, would wait for ALL loads in
 //   flight (vmcnt(0)) and serialise the ring.
@@ -47,7 +50,7 @@
 //   ~45 % of LDS cycles in bank conflicts).
 // * P1 takes a whole CU (12 waves, up to 157 KB of LDS: 8 matrix waves and 4
 //   producer waves that load and convert); the 128-token P3 takes a whole CU
-//   too (8 waves, 160 KB), the 16-column one 4 waves and 36 KB.
+//   too (8 waves, 160 KB), the narrow one 4 waves and 48-64 KB.
 // * XCD-aware grids (workgroup b runs on XCD b % 8): with 8 splits P1's XCD x
 //   owns split x, so its 820 KB W_down slice stays in that XCD's L2; P3's XCD
 //   x owns 5 of the 40 column groups (W_up slices, 820 KB) and walks the token
@@ -852,7 +855,7 @@ __global__ __launch_bounds__(256, 2) void prefill_upmix(int T, const uint4* __re
     constexpr int kCols = 16 * CB;                      // output columns of the tile
     constexpr int kGpx = kWidth / kCols / 8;            // column groups per XCD (20 / CB)
     constexpr int kUpWChunks = 4 * kCols * 4;           // W_up panel: 256 CB chunks
-    constexpr int kUpStage = kUpWChunks + kLoTile;      // 768 chunks
+    constexpr int kUpStage = kUpWChunks + kLoTile;      // 256 CB + 512 chunks
     constexpr int kUpLoads = kUpStage / 64 / 4;         // wave instructions per stage and wave (2 + CB)
     constexpr int NB = 2 * CB;                          // panel blocks of two streams
     static_assert(NS >= 3 && NS <= kUpSteps && (CB == 1 || CB == 2), "stages, column blocks");
