@@ -635,20 +635,58 @@ __global__ __launch_bounds__(512) void prefill_down_small(int T, const float* __
                 acc[mb][pc] = mfma16(a[mb], bb[pc], acc[mb][pc]);
     }
     ring_barrier<0>();  // every wave's second lines in LDS
-    // K steps 2-3, block by block; the partial dots of block mb - 1 are
-    // stored (written through, sc1: they drain while other workgroups
-    // compute instead of all at the end of the launch from the L2s) while
-    // block mb's products run
+    // K steps 2-3, block by block; the partial dots of the blocks before
+    // block mb are stored (written through, sc1: they drain while other
+    // workgroups compute instead of all at the end of the launch from the
+    // L2s) while block mb's products run.  Two blocks that make up a token's
+    // 128-byte line (blocks mb, mb + 1 with mb - ps even) are stored as whole
+    // lines: lanes n and n ^ 8 (DPP row_ror:8) trade halves, so one store
+    // instruction writes 8 tokens x 128 bytes instead of 16 tokens x 64.
     const int t = t0 + 16 * th + n;
     const __amdgpu_buffer_rsrc_t prs = rsrc_of(part);
     const uint32_t dst = 4u * (uint32_t)(((size_t)sig * T + (t < T ? t : 0)) * kRank + RW * rg + 4 * g);
-    auto store_block = [&](int mb) {
+    const int ta = t0 + 16 * th + (n & 7), tb = ta + 8;  // the tokens of a lane's two whole-line stores
+    const uint32_t dsta = 4u * (uint32_t)(((size_t)sig * T + (ta < T ? ta : 0)) * kRank + RW * rg + 4 * g);
+    const uint32_t dstb = 4u * (uint32_t)(((size_t)sig * T + (tb < T ? tb : 0)) * kRank + RW * rg + 4 * g);
+    const int ps = ((RW * rg) >> 4) & 1;  // parity of the first block that starts a 128-byte line
+    auto block_sum = [&](int mb) {
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             v[e] = acc[mb][0][e] + (acc[mb][1][e] + acc[mb][2][e]);
+        return v;
+    };
+    auto store_single = [&](int mb) {
+        const f32x4_t v = block_sum(mb);
         if (t < T)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs, dst + 64u * mb, 0, 16 /* sc1 */);
+    };
+    auto store_pair = [&](int mb) {
+        const f32x4_t va = block_sum(mb), vb = block_sum(mb + 1);
+        const bool low = n < 8;
+        f32x4_t s1, s2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = low ? vb[e] : va[e];  // the half the partner lane stores
+            const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, true));
+            s1[e] = low ? va[e] : y;  // token ta: block mb (lanes n < 8), block mb + 1 (n >= 8)
+            s2[e] = low ? y : vb[e];  // token tb: likewise
+        }
+        const uint32_t half = low ? 0u : 64u;
+        if (ta < T)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s1), prs, dsta + 64u * mb + half, 0, 16);
+        if (tb < T)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s2), prs, dstb + 64u * mb + half, 0, 16);
+    };
+    // stores what block p completes: nothing if it starts a line (its partner
+    // follows), the pair if it ends one, else the block alone
+    auto flush = [&](int p) {
+        const bool second = ((p - ps) & 1) != 0 && p >= 1;
+        const bool first = ((p - ps) & 1) == 0 && p + 1 < MB;
+        if (second)
+            store_pair(p - 1);
+        else if (!first)
+            store_single(p);
     };
     u32x4 b2[2][3];
 #pragma unroll
@@ -673,9 +711,9 @@ __global__ __launch_bounds__(512) void prefill_down_small(int T, const float* __
             for (int pc = 0; pc < 3; ++pc)
                 acc[mb][pc] = mfma16(a2[h], b2[h][pc], acc[mb][pc]);
         if (mb > 0)
-            store_block(mb - 1);
+            flush(mb - 1);
     }
-    store_block(MB - 1);
+    flush(MB - 1);
 #pragma unroll
     for (int k = 0; k < NPASS; ++k) {
         const int tl = (tid >> 4) + 32 * k;
