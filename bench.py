@@ -241,7 +241,7 @@ def main():
           file=sys.stderr, flush=True)
     del floor_bufs
 
-    # ---- reads of 9..512 tokens (up to 32: one short-window launch; beyond:
+    # ---- reads of 9..512 tokens (up to 25: one short-window launch; beyond:
     # the wide path), eager, weights rotated over the 48 sets.  Every input
     # is made first, and the reads run after WARM_STEP_MS of GPU time of
     # window reads, so that no host-side pause between two token counts

@@ -113,7 +113,7 @@ def hc_read_bf16_lo(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, ou
 
 
 def hc_read_noalloc(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, out_fp16, stream=None):
-    """hc_read_noalloc of the C ABI: hc_read for T <= 32 without any device
+    """hc_read_noalloc of the C ABI: the short-window read for T <= 32 without any device
     allocation (after hc_short_window_on() on the device).
 
     Returns the status code (0 = HC_OK)."""
@@ -123,7 +123,7 @@ def hc_read_noalloc(T, R, pending, w_norm, W_down, W_up, out_mixed, out_bf16, ou
 
 
 def hc_short_window_on() -> bool:
-    """Whether the current device reads windows of up to 32 tokens with the
+    """Whether the current device reads short windows (up to 25 tokens; 32 without allocation) with the
     short-window kernel (the library's start-up check decides; it runs now if
     it has not yet)."""
     on = ctypes.c_int()

@@ -1,7 +1,8 @@
 // hc_api.hip -- host side of the C ABI declared in include/hc.h: argument
 // checks, per-(device, stream) scratch workspaces, the start-up check of the
-// short-window kernel, and dispatch to the short-window (T <= 32, one launch)
-// and wide (prefill) kernels.
+// short-window kernel, and dispatch to the short-window (one launch, up to 25
+// tokens from hc_read, up to 32 from hc_read_noalloc) and wide (prefill)
+// kernels.
 #include "hc.h"
 #include "hc_internal.h"
 
@@ -208,7 +209,7 @@ struct CheckRng {
 // wide path (which needs neither) and keeps it only if (a) every workgroup
 // fits, (b) no bounded wait expired and (c) each pair of outputs agrees to
 // 4e-6 of its largest value (each is within 2e-6 of the exact read).
-// Otherwise windows of up to 32 tokens take the wide path.  The bounded
+// Otherwise every read takes the wide path.  The bounded
 // waits' limit can be lowered with HC_SELFCHECK_WAIT_TICKS (ticks of the 100
 // MHz clock) to force the fallback.  One line per device goes to stderr
 // (HC_LOG=0 silences it).
@@ -304,7 +305,7 @@ int run_short_window_check(int dev, Workspace* ws, bool* on, char* why, size_t w
     return HC_OK;
 }
 
-// Whether windows of up to 32 tokens use the short-window kernel on `dev`;
+// Whether short windows use the short-window kernel on `dev`;
 // the check runs on the first call for the device.
 int short_window_on(int dev, Workspace* ws, bool* on)
 {
@@ -335,7 +336,7 @@ int short_window_on(int dev, Workspace* ws, bool* on)
     g_short_window.emplace(dev, *on);
     if (log_enabled())
         std::fprintf(stderr, "hc: device %d: the short-window read is %s (start-up check: %s)%s\n", dev,
-                     *on ? "on" : "OFF", why, *on ? "" : "; windows of up to 32 tokens take the wide path");
+                     *on ? "on" : "OFF", why, *on ? "" : "; every read takes the wide path");
     return HC_OK;
 }
 
@@ -417,7 +418,7 @@ int read_impl(int64_t T, const float* R, const float* pending, const float* w_no
     if (st != HC_OK)
         return st;
 
-    if (T <= hc::kDecMaxT && short_ok) {
+    if (T <= hc::kShortReadMaxT && short_ok) {
         hipError_t e = launch_short_window(dev, hs, static_cast<int>(T), R, pending, w_norm, W_down, W_up,
                                            out_mixed, out_bf16, out_fp16, R_commit, ws->dec);
         return e == hipSuccess ? HC_OK : record(e, HC_ERR_LAUNCH);

@@ -31,6 +31,13 @@ constexpr float kEps = 1e-6f;
 // polled by the consumer.
 // ---------------------------------------------------------------------------
 constexpr int kDecMaxT = 32;
+// hc_read and its variants run the short-window kernel up to this many
+// tokens and the wide path above: from 26 tokens the wide path is the faster
+// one (measured back to back at 26 / 28 / 30 / 32 tokens: 14.8 / 15.0 /
+// 15.0 / 15.2 us against 15.2 / 15.6 / 16.0 / 16.1 us; at 25 they tie).
+// The kernel itself takes up to kDecMaxT (hc_read_noalloc and the start-up
+// check run it up to 32).
+constexpr int kShortReadMaxT = 25;
 constexpr int kDecWGs = 256;
 constexpr int kDecThreads = 512;
 constexpr int kDecXcds = 8;

@@ -1,4 +1,4 @@
-// hc_prefill.hip -- the hyper-connection read for wide inputs (T > 32 tokens):
+// hc_prefill.hip -- the hyper-connection read for wide inputs (T > 25 tokens):
 // prefill chunks and verify windows beyond the short-window kernel.
 //
 // The read is the one of "#315 hc: the multi-token hyper-connection read split

@@ -39,7 +39,8 @@
  * a later stream that HIP gives the same handle takes it over, which is safe
  * once the old stream's work has finished).  Calls on different streams never
  * share scratch.  Calls on ONE stream are ordered by the stream and are safe.
- * Short-window reads (T <= 32) use every CU of the device and must not run at
+ * Short-window reads (hc_read and its variants up to 25 tokens, hc_read_noalloc
+ * up to 32) use every CU of the device and must not run at
  * the same time: the library orders them across streams.  A short-window
  * read on another stream than the device's last one waits for that last
  * read: through an event recorded right after it if there is one, else by
@@ -113,8 +114,8 @@ extern "C" {
  *              (subnormals kept, overflow to +-inf)
  *   stream     hipStream_t to run on (NULL = default stream)
  *
- * T <= 32 runs one launch of the short-window (verify-window) kernel; larger
- * T runs the wide (prefill) path.  The short-window kernel is
+ * T <= 25 runs one launch of the short-window (verify-window) kernel; larger
+ * T runs the wide (prefill) path, which is the faster one from 26 tokens.  The short-window kernel is
  * used only where its start-up check passed (see hc_short_window_on);
  * elsewhere every T runs the wide path.  Every valid T is handled; there is no
  * fallback to return.
@@ -155,7 +156,7 @@ HC_API int hc_read_commit(int64_t T, float* R, const float* pending, const float
  * "#1370 prefill: opt-in STRATA_HC_UPMIX=1 on CUDA", What it does (BF16 mma
  * with FP32 accumulation), instead of the exact three-piece split of lo.  The
  * norm, the down projection and lo itself are unchanged, and windows of up to
- * 32 tokens (the short-window kernel) give hc_read's result.
+ * 25 tokens (the short-window kernel) give hc_read's result.
  * Its contract is an error bound, not hc_read's 2e-6: every mixed value is
  * within 2^-8 * sum_s |R'[t][s][c]| * sum_j |W_up[s*2560+c][j]| * |lo[t][j]|
  * of the exact read (the bf16 rounding of each lo value), plus hc_read's
@@ -172,8 +173,10 @@ HC_API int hc_read_bf16_lo(int64_t T, const float* R, const float* pending, cons
  * routine: the hand-off scratch of the short-window kernel lives in a
  * file-scope device array of 3.7 MB that each GPU the library runs on holds
  * until the process ends, and every allocation-free read of a device shares
- * it.  Arguments, layouts and results are hc_read's (the same kernel, the
- * same bits); the caller still passes inputs and outputs.
+ * it.  Arguments and layouts are hc_read's; the caller still passes inputs
+ * and outputs.  Up to 25 tokens the results are hc_read's bits (the same
+ * kernel); from 26 to 32 tokens it runs the short-window kernel where hc_read
+ * takes the wide path, and the two agree within hc_read's 2e-6.
  *
  * Limit: T <= 32 (one short-window launch); a larger T returns HC_ERR_SIZE
  * and enqueues nothing.  Set-up: the device's start-up check (the first
@@ -191,8 +194,9 @@ HC_API int hc_read_noalloc(int64_t T, const float* R, const float* pending, cons
                            uint16_t* out_bf16, uint16_t* out_fp16, void* stream);
 
 /*
- * hc_short_window_on -- *on = 1 if the current device reads windows of up to
- * 32 tokens with the short-window kernel, 0 if they take the wide path.  The
+ * hc_short_window_on -- *on = 1 if the current device reads short windows
+ * with the short-window kernel (hc_read up to 25 tokens, hc_read_noalloc up
+ * to 32), 0 if every read takes the wide path.  The
  * kernel's hand-offs need its 256 workgroups resident together and placed on
  * the XCDs the way it expects; once per device (on the first call of any
  * entry point that reads) the library reads windows of 1, 5, 9, 17 and 32

@@ -76,8 +76,9 @@ def test_windows_of_9_to_16_every_count():
 
 
 def test_windows_of_17_to_32_every_count():
-    """Every token count of the six-chain range (32 token slots, LDS regions
-    shared between phases), with pending.  Full oracle."""
+    """Every token count from 17 to 32, with pending: 17..25 on the six-chain
+    short-window kernel (32 token slots, LDS regions shared between phases),
+    26..32 on the wide path (the faster one there).  Full oracle."""
     for T in range(17, 33):
         _case("window of %d tokens, pending, weight set 22" % T)
         inp = wl.config_inputs(2, T=T, weight_set=22)
@@ -101,12 +102,12 @@ def test_ragged_token_counts(T):
     assert_parity(gpu, _oracle(inp), label="T=%d" % T)
 
 
-@pytest.mark.parametrize("T, pending", [(9, True), (12, False), (16, True), (17, True), (24, False), (32, True),
-                                        (33, True)])
+@pytest.mark.parametrize("T, pending", [(9, True), (12, False), (16, True), (17, True), (24, False), (25, False),
+                                        (26, False), (32, True), (33, True)])
 def test_windows_above_eight(T, pending):
     """9..16 tokens run as one short-window launch with three MFMA chains and
-    16 token slots per partial row, 17..32 with six chains and 32 slots; 33
-    is the first count on the wide path.  Full oracle."""
+    16 token slots per partial row, 17..25 with six chains and 32 slots; 26
+    is the first count hc_read sends to the wide path.  Full oracle."""
     _case("window of %d tokens, pending=%s" % (T, pending))
     inp = wl.config_inputs(2, T=T, weight_set=5)
     if not pending:
@@ -115,11 +116,12 @@ def test_windows_above_eight(T, pending):
     assert_parity(gpu, _oracle(inp), label="T=%d pending=%s" % (T, pending))
 
 
-@pytest.mark.parametrize("T, half", [(32, 16), (20, 10)])
+@pytest.mark.parametrize("T, half", [(24, 12), (20, 10)])
 def test_window_equals_its_halves(T, half):
     """Above 8 tokens a token's arithmetic does not depend on the window: the
-    six-chain kernel (17..32 tokens) gives every token the bits that the
-    three-chain kernel gives it in a window of half the size."""
+    six-chain kernel (17..25 tokens from hc_read) gives every token the bits
+    that the three-chain kernel gives it in a window of half the size (26..32
+    tokens, which only hc_read_noalloc runs on this kernel: its own test)."""
     _case("T=%d against two T=%d reads of its halves" % (T, half))
     inp = wl.config_inputs(2, T=T, weight_set=9)
     whole = hip_read(to_device(inp))
@@ -181,7 +183,7 @@ def test_forced_check_failure_falls_back_to_the_wide_path():
     """With the bounded waits' limit forced to 0 ticks for the start-up check
     (every wait of the check's read gives up at its first miss, and the
     kernel still ends normally), the check fails, the library logs it, and
-    windows of up to 32 tokens then run the wide path, still at parity.  Run
+    every read then runs the wide path, still at parity.  Run
     in a child process, since the check runs once per process."""
     import os
     import subprocess
@@ -403,7 +405,7 @@ def test_release_stream_then_read_again():
 
 
 def test_bf16_lo_mode_short_windows_are_exact():
-    """Up to 32 tokens hc_read_bf16_lo is the short-window read: hc_read's bits."""
+    """Up to 25 tokens hc_read_bf16_lo is the short-window read: hc_read's bits."""
     _case("bf16-lo mode at T=8 and T=24 against hc_read")
     for T in (8, 24):
         dev = to_device(wl.config_inputs(2, T=T, weight_set=6))

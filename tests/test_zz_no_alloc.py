@@ -1,7 +1,10 @@
 """hc_read_noalloc, the allocation-free entry point, through the C ABI against
-hc_read on the same inputs: the same kernel, so the same bits (and hc_read is
-held to the oracle elsewhere).  Two calls in a row, the second smaller; a
-capture on a stream that never allocated; and the size limit."""
+hc_read on the same inputs: up to 25 tokens the same kernel, so the same bits
+(and hc_read is held to the oracle elsewhere); from 26 to 32 tokens, where
+hc_read takes the wide path, against two hc_read reads of the window's parts
+(above 8 tokens a token's bits do not depend on the window).  Two calls in a
+row, the second smaller; a capture on a stream that never allocated; and the
+size limit."""
 import numpy as np
 import pytest
 
@@ -48,7 +51,7 @@ def _same(got, ref, label):
                               b.view(np.uint32) if b.dtype == np.float32 else b), label
 
 
-@pytest.mark.parametrize("sizes, pending", [((24, 5), True), ((32, 1), False), ((9, 8), True)])
+@pytest.mark.parametrize("sizes, pending", [((24, 5), True), ((25, 1), False), ((9, 8), True)])
 def test_noalloc_matches_hc_read_on_two_calls(sizes, pending):
     import torch
     devs, refs = [], []
@@ -65,6 +68,29 @@ def test_noalloc_matches_hc_read_on_two_calls(sizes, pending):
     torch.cuda.synchronize()
     for k, (o, ref) in enumerate(zip(outs, refs)):
         _same(o, ref, "call %d (T=%d)" % (k, sizes[k]))
+
+
+def test_noalloc_windows_of_26_to_32_equal_their_parts():
+    """26..32 tokens, which hc_read sends to the wide path: hc_read_noalloc (the
+    six-chain short-window kernel) gives every token the bits of hc_read reads
+    of the window's two parts (13..16 tokens each, the three-chain kernel)."""
+    import dataclasses
+    import torch
+    for T in range(26, 33):
+        _case("hc_read_noalloc T=%d against hc_read of its parts" % T)
+        inp = wl.config_inputs(2, T=T, weight_set=30 + T)
+        o = _outputs(T)
+        assert _noalloc(to_device(inp), o) == 0
+        torch.cuda.synchronize()
+        got = (o[0].cpu().numpy(), o[1].cpu().numpy().view(np.uint16), o[2].cpu().numpy().view(np.uint16))
+        a = T // 2
+        for lo, hi in ((0, a), (a, T)):
+            part = dataclasses.replace(inp, R=inp.R[lo:hi].copy(), pending=inp.pending[lo:hi].copy())
+            ref = hip_read(to_device(part))
+            for x, y in zip(ref, got):
+                assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                                      (y.view(np.uint32) if y.dtype == np.float32 else y)[lo:hi]), \
+                    "T=%d tokens %d..%d" % (T, lo, hi - 1)
 
 
 def test_noalloc_under_capture_on_a_stream_that_never_allocated():
