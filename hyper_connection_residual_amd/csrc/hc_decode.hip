@@ -382,6 +382,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
     return (uint32_t)(uintptr_t)p;  // the low 32 bits of a shared-aperture address are the LDS offset
 }
+__device__ __forceinline__ void ds_st16(const void* p, uint32_t v)
+{
+    asm volatile("ds_write_b16 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
 __device__ __forceinline__ void ds_st32(const void* p, uint32_t v)
 {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
@@ -552,8 +556,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
         }
     }
-    // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c)
-    //     and R and pending of those 40 (stream, column) pairs, for the mix.
+    // (4) later: the W_up tile (tile row 4 c + s = W_up row s * 2560 + c0 + c;
+    //     buffer loads into LDS, unrolled like the W_down tile's, which the
+    //     compiler counts exactly where after global_load_lds it would wait
+    //     for every load before the first use of a polled word) and R and
+    //     pending of those 40 (stream, column) pairs, for the mix.
     //     Above 8 tokens thread j's pass pp holds item j + 512 pp = 40 t + row
     //     (staged through LDS); in the quad layout lane (n, g) of wave w < 3
     //     holds, in slot c, token 4 c + g of the tile row its up products
@@ -562,10 +569,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     float mr[kUpPasses], mp[kUpPasses];
     const int up_row = wave < 2 ? 16 * wave + n : 32 + (n & 7);  // (quad layout, waves 0..2)
     auto issue_up = [&]() {
-        for (int q = wave; q < kTileInstr; q += 8) {
-            int row, j;
-            tile_lane<kRowChunks>(q, lane, row, j);
-            dma16(W_up + (size_t)((row & 3) * kWidth + c0 + (row >> 2)) * kRank + 8 * j, utile + 64 * q);
+        const __amdgpu_buffer_rsrc_t wur = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(W_up), 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int q = wave + 8 * k;
+            if (k < 3 || wave == 0) {
+                int row, j;
+                tile_lane<kRowChunks>(q, lane, row, j);
+                bdma16(wur, utile + 64 * q, 2u * ((uint32_t)((row & 3) * kWidth + c0 + (row >> 2)) * kRank + 8 * j));
+            }
         }
         if constexpr (kQuad<T>) {
             if (wave < 3) {
@@ -942,7 +955,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     {
         // (10) hop 2: wave w polls the lo words of XCD w's reducers (slot =
         //     reducer, token, pair of rows) until every tag is current, then
-        //     stages the 3 bf16 pieces of each value.  (Waves start after this
+        //     stages the 3 bf16 pieces of each value (inline-asm LDS stores,
+        //     which do not wait for the W_up tile still landing).  (Waves start after this
         //     workgroup's own reducer is done, so their cold loads do not
         //     queue in front of its L2 polls.)
         constexpr int NSL = kDecReducers * T * 2;  // slots per wave
@@ -1011,9 +1025,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                         const int jr = kDecRowsPerXcd * wave + rowl;
                         uint32_t hb, mb, lb;
                         split3(__uint_as_float(h ? lw[k].z : lw[k].x), hb, mb, lb);
-                        lpl[plane_row<T>(0, tt) * kLoRow + jr] = (uint16_t)hb;
-                        lpl[plane_row<T>(1, tt) * kLoRow + jr] = (uint16_t)mb;
-                        lpl[plane_row<T>(2, tt) * kLoRow + jr] = (uint16_t)lb;
+                        ds_st16(&lpl[plane_row<T>(0, tt) * kLoRow + jr], hb);
+                        ds_st16(&lpl[plane_row<T>(1, tt) * kLoRow + jr], mb);
+                        ds_st16(&lpl[plane_row<T>(2, tt) * kLoRow + jr], lb);
                     }
                 }
             }
