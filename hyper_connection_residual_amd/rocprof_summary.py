@@ -66,7 +66,9 @@ def stats(path: str) -> str:
 
 def _clusters(d):
     """Sorted durations split where one is more than 1.6x the one before (a
-    persistent kernel launched at several read sizes keeps its grid)."""
+    persistent kernel launched at several read sizes keeps its grid); a group
+    of fewer than 3 durations is an outlier of the group below it, not a size
+    of its own."""
     d = sorted(d)
     out, cur = [], [d[0]]
     for v in d[1:]:
@@ -74,7 +76,10 @@ def _clusters(d):
             out.append(cur)
             cur = []
         cur.append(v)
-    out.append(cur)
+    if out and len(cur) < 3:
+        out[-1].extend(cur)
+    else:
+        out.append(cur)
     return out
 
 
